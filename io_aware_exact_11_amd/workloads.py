@@ -1,0 +1,117 @@
+"""Seeded synthetic inputs for the attention workloads.
+
+This module only draws random numbers and rounds them to the storage type.
+It holds none of the attention arithmetic, so both the fp64 oracle (through
+the tests) and the HIP path can be fed from it without sharing any part of
+the method.
+
+Recipe (one numpy PCG64 stream per workload, seeded with the workload's
+seed):
+  1. draw float32 standard normals in C order for Q, K, V, dO, each
+     [B, H, N, d], in that order;
+  2. multiply Q, K, V by ``qkv_scale`` (0.5 for the N=4096, d=128 workload);
+  3. padded workloads then draw one valid length per batch row,
+     kv_len[b] ~ U{N/2 .. N} (both ends included), and one outlier key per
+     (b, h), uniform over the valid keys, whose K row is multiplied by 8;
+  4. bf16 workloads round every tensor to bfloat16 with round-to-nearest-even.
+
+The shapes follow the pages' workloads: the GPT-2-medium attention shape
+(FlashAttention does more arithmetic to move less data, section
+"FlashAttention never writes the full score table to HBM"), the N=4096,
+d=128 head of FlashAttention and GPU Memory chapter 04, and long and padded
+batches for the linear-memory and masking claims.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    dtype: str            # "bf16" or "fp32": storage type of Q, K, V, dO
+    causal: tuple         # causal variants this workload is run in
+    padded: bool          # per-batch key-padding lengths + one outlier key
+    qkv_scale: float
+    seed: int
+    note: str = ""
+
+    @property
+    def scale(self) -> float:
+        """Softmax scale 1/sqrt(d), as the fp32 value both sides receive."""
+        return float(np.float32(1.0 / math.sqrt(self.d)))
+
+
+WORKLOADS = {
+    "tiny_fp32": Workload("tiny_fp32", 1, 1, 128, 64, "fp32", (False,), False, 1.0, 1,
+                          "single head, fp32, non-causal"),
+    "gpt2_medium": Workload("gpt2_medium", 64, 16, 1024, 64, "bf16", (True,), False, 1.0, 2,
+                            "GPT-2-medium-shaped attention, causal"),
+    "n4096_d128": Workload("n4096_d128", 16, 16, 4096, 128, "bf16", (False, True), False, 0.5, 3,
+                           "N=4096, d=128, causal and non-causal, Q/K/V scaled by 0.5"),
+    "long_16k": Workload("long_16k", 2, 16, 16384, 128, "bf16", (True,), False, 1.0, 4,
+                         "long context, causal"),
+    "padded_8k": Workload("padded_8k", 8, 32, 8192, 64, "bf16", (False,), True, 1.0, 5,
+                          "key padding with kv_len ~ U[N/2, N] and one x8 outlier key per head"),
+}
+
+
+def bf16_round_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns (uint16), round to nearest even."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return rounded.astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) -> exactly equal float32 values."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def make_inputs(B: int, H: int, N: int, d: int, seed: int, dtype: str = "bf16",
+                qkv_scale: float = 1.0, padded: bool = False) -> dict:
+    """Draw Q, K, V, dO (and kv_len when padded) following the module recipe.
+
+    Returns a dict with float32 arrays "Q", "K", "V", "dO" holding exactly the
+    values the kernels see (already rounded when dtype is bf16), the uint16 bit
+    patterns under "Q_bits" etc. for bf16, and "kv_len" (int32 [B]) or None.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    shape = (B, H, N, d)
+    out = {}
+    for name in ("Q", "K", "V", "dO"):
+        out[name] = rng.standard_normal(size=shape, dtype=np.float32)
+    if qkv_scale != 1.0:
+        for name in ("Q", "K", "V"):
+            out[name] *= np.float32(qkv_scale)
+    kv_len = None
+    if padded:
+        kv_len = rng.integers(N // 2, N, endpoint=True, size=B).astype(np.int32)
+        for b in range(B):
+            idx = rng.integers(0, kv_len[b], size=H)
+            for h in range(H):
+                out["K"][b, h, idx[h], :] *= np.float32(8.0)
+    out["kv_len"] = kv_len
+    if dtype == "bf16":
+        for name in ("Q", "K", "V", "dO"):
+            bits = bf16_round_bits(out[name])
+            out[name + "_bits"] = bits
+            out[name] = bf16_bits_to_f32(bits)
+    elif dtype != "fp32":
+        raise ValueError(f"unknown dtype {dtype!r}")
+    return out
+
+
+def workload_inputs(name: str, **overrides) -> dict:
+    """Inputs of a named workload; keyword overrides replace B, H, N or d."""
+    w = WORKLOADS[name]
+    dims = {k: overrides.get(k, getattr(w, k)) for k in ("B", "H", "N", "d")}
+    return make_inputs(dims["B"], dims["H"], dims["N"], dims["d"], w.seed, w.dtype,
+                       w.qkv_scale, w.padded)
