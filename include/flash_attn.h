@@ -1,0 +1,120 @@
+/*
+ * flash_attn.h -- C ABI of libflashattn.so: exact attention forward and
+ * backward on one AMD Instinct MI355X (gfx950).
+ *
+ * The forward computes O = softmax(scale * Q K^T + mask) V block by block
+ * with a running softmax, so the N x N score and probability matrices never
+ * reach device memory, and saves one log-sum-exp value per query row
+ * ("FlashAttention and GPU Memory", chapters 07 Blocks and 08 A softmax with
+ * a running tally; "48 FlashAttention", the sdpa snippet, for the
+ * 1/sqrt(d) scaling). The backward rebuilds the score and probability tiles
+ * from Q, K, V and the saved row statistics instead of reading a stored P
+ * ("FlashAttention and GPU Memory", chapter 09 Backward: recomputing beats
+ * reading; "FlashAttention does more arithmetic to move less data", section
+ * "FlashAttention never writes the full score table to HBM", move 4).
+ *
+ * Conventions shared by every entry point:
+ *   - Tensors are dense, row-major [B, H, N, d] with d innermost (element
+ *     (b,h,n,c) at ((b*H + h)*N + n)*d + c). LSE and the backward workspace
+ *     rows are [B, H, N].
+ *   - All tensor pointers are DEVICE pointers, owned by the caller. The
+ *     library allocates nothing, keeps no state between calls and never
+ *     synchronises; every kernel is enqueued on `stream` (a hipStream_t,
+ *     NULL = the default stream). Outputs must not alias inputs or each other.
+ *   - Masking: key j is visible to query i iff j < kv_len[b] (when kv_len is
+ *     not NULL) and, when causal != 0, j <= i (top-left aligned,
+ *     self-attention: the query and key sequences have the same length N).
+ *     kv_len is a DEVICE array of B int32 values; values outside [0, N] are
+ *     clamped to it by the kernels. A query row with no visible key gets
+ *     O = 0, LSE = -inf and contributes no gradient.
+ *   - scale multiplies the scores; it must be finite and > 0 (1/sqrt(d) is
+ *     the usual value).
+ *   - d must be 64 or 128; N, B, H >= 1; B*H*N*d must fit in a signed
+ *     32-bit element index.
+ *   - Arguments are checked on the host before anything is enqueued; a bad
+ *     argument returns FA_ERR_INVALID_ARG (or FA_ERR_UNSUPPORTED for a
+ *     well-formed request this build does not implement) and launches
+ *     nothing. A failed launch returns FA_ERR_HIP. Faults inside a kernel
+ *     surface at the caller's next synchronisation.
+ */
+#ifndef FLASH_ATTN_H
+#define FLASH_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = 1,
+  FA_ERR_UNSUPPORTED = 2,
+  FA_ERR_HIP = 3
+} fa_status;
+
+/* flash_attn_bwd flags. */
+enum {
+  /* Compute the per-row term sum_j P_ij dP_ij exactly, by an extra pass that
+   * recomputes the score and dP tiles, instead of from the bf16-rounded
+   * output as rowsum(dO * O); and feed P and dS to the gradient products as
+   * a bf16 high/low pair. Slower (about twice the matrix work), for inputs
+   * whose gradients are large (e.g. outlier keys), where bf16 rounding of
+   * O, P and dS dominates the error. */
+  FA_BWD_PRECISE = 1u << 0
+};
+
+/*
+ * Forward, bf16. Q, K, V: bf16 [B,H,N,d]. O: bf16 [B,H,N,d] output,
+ * normalised. LSE: float [B,H,N] output, natural log:
+ * LSE_i = ln sum_j exp(scale * q_i . k_j) over visible j.
+ * Scores, the running maximum and sum, and both products accumulate in
+ * fp32; P is rounded to bf16 only as the operand of the P V product.
+ */
+int flash_attn_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                   int B, int H, int N, int d, float scale, int causal,
+                   const int32_t* kv_len, void* stream);
+
+/*
+ * Backward, bf16 inputs, fp32 gradients. Q, K, V, O, dO: bf16 [B,H,N,d]
+ * (O and LSE exactly as flash_attn_fwd wrote them). dQ, dK, dV: float
+ * [B,H,N,d] outputs, fully overwritten. workspace: device memory of at least
+ * flash_attn_bwd_workspace_bytes(B,H,N,d,flags) bytes, 256-byte aligned,
+ * used for the per-row term D_i = sum_j P_ij dP_ij; its contents on entry
+ * do not matter. flags: 0 or FA_BWD_PRECISE; any other bit is
+ * FA_ERR_INVALID_ARG. dQ is accumulated with fp32 atomics, so it is not
+ * bitwise reproducible from run to run; dK and dV are.
+ */
+int flash_attn_bwd(const void* Q, const void* K, const void* V, const void* O,
+                   const void* dO, const float* LSE, float* dQ, float* dK, float* dV,
+                   void* workspace, size_t workspace_bytes,
+                   int B, int H, int N, int d, float scale, int causal,
+                   const int32_t* kv_len, unsigned flags, void* stream);
+
+/* Workspace bytes flash_attn_bwd / flash_attn_bwd_f32 need (0 for bad sizes). */
+size_t flash_attn_bwd_workspace_bytes(int B, int H, int N, int d, unsigned flags);
+
+/*
+ * fp32 twins: identical argument lists and semantics with float Q, K, V, O,
+ * dO. Every step runs in fp32 on the vector ALUs (no matrix cores); meant
+ * for small single-precision problems and as a precision reference path.
+ * flash_attn_bwd_f32 accepts flags == 0 only.
+ */
+int flash_attn_fwd_f32(const float* Q, const float* K, const float* V, float* O, float* LSE,
+                       int B, int H, int N, int d, float scale, int causal,
+                       const int32_t* kv_len, void* stream);
+int flash_attn_bwd_f32(const float* Q, const float* K, const float* V, const float* O,
+                       const float* dO, const float* LSE, float* dQ, float* dK, float* dV,
+                       void* workspace, size_t workspace_bytes,
+                       int B, int H, int N, int d, float scale, int causal,
+                       const int32_t* kv_len, unsigned flags, void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* flash_attn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLASH_ATTN_H */

@@ -1,0 +1,369 @@
+// Backward pass of exact attention for gfx950: bf16 inputs, fp32 gradients.
+//
+// The forward kept only O and one log-sum-exp per row; here the score and
+// probability tiles are rebuilt block by block from Q, K, V
+// ("FlashAttention and GPU Memory", chapter 09 Backward: recomputing beats
+// reading; "FlashAttention does more arithmetic to move less data", move 4).
+// With P_ij = exp(s q_i.k_j - LSE_i) the gradients are, by the chain rule,
+//   dV = P^T dO,  dP = dO V^T,  dS = P o (dP - D),  dK = s dS^T Q,  dQ = s dS K,
+// where D_i = sum_j P_ij dP_ij. Since O = P V, D_i equals dO_i . O_i, which a
+// bandwidth-bound pre-pass computes from O and dO (default), or, with
+// FA_BWD_PRECISE, a separate recompute pass sums P o dP exactly.
+//
+// Main kernel (one workgroup per 128 keys of one (b, h), 4 waves of 32 keys):
+//   * the wave's K and V rows sit in registers as the B operands of
+//     S = Q K^T and dP = dO V^T (32x32x16 bf16 products, fp32 accumulate);
+//   * query blocks of 64 rows stream through LDS, stored both row-major
+//     (A operand of S and dP) and transposed (A operand of dV^T = dO^T P and
+//     dK^T = Q^T dS, whose B operands are the P and dS registers themselves);
+//   * dV^T and dK^T for the wave's keys accumulate in registers across all
+//     query blocks and are written once;
+//   * dS goes to LDS, and the workgroup adds dQ_i += s dS K for its 128 keys
+//     into the fp32 dQ output with hardware float atomics.
+// Causal workgroups start at the first query block that can see their keys;
+// waves whose keys are all invisible to a block skip its products.
+#include "fa_common.h"
+#include "fa_launch.h"
+
+namespace fa {
+
+// ---------------------------------------------------------------- helpers
+
+__global__ void fill_zero_kernel(float4* __restrict__ p, size_t n4) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride)
+    p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+static hipError_t fill_zero(float* p, size_t n, hipStream_t stream) {
+  const size_t n4 = n / 4;  // n is a multiple of 4 (d in {64, 128})
+  size_t blocks = (n4 + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  if (blocks == 0) blocks = 1;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     reinterpret_cast<float4*>(p), n4);
+  return hipGetLastError();
+}
+
+// D_i = sum_c dO[i,c] * O[i,c] in fp32 from the bf16 tensors; 16 lanes per row.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dot_kernel(const u16* __restrict__ O,
+                                                      const u16* __restrict__ dO,
+                                                      float* __restrict__ Dout, int rows) {
+  constexpr int EPL = D / 16;  // elements per lane: 8 or 4
+  const int gid = blockIdx.x * 256 + threadIdx.x;
+  const int row = gid >> 4, sub = gid & 15;
+  float acc = 0.f;
+  if (row < rows) {
+    const size_t off = (size_t)row * D + sub * EPL;
+    if constexpr (EPL == 8) {
+      const u32x4 a = ld_global16(O + off), c = ld_global16(dO + off);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        acc += __uint_as_float(bf16_bits(a, e) << 16) * __uint_as_float(bf16_bits(c, e) << 16);
+    } else {
+      const u32x2 a = *reinterpret_cast<const u32x2*>(O + off);
+      const u32x2 c = *reinterpret_cast<const u32x2*>(dO + off);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const unsigned ab = (a[e >> 1] >> ((e & 1) * 16)) & 0xffffu;
+        const unsigned cb = (c[e >> 1] >> ((e & 1) * 16)) & 0xffffu;
+        acc += __uint_as_float(ab << 16) * __uint_as_float(cb << 16);
+      }
+    }
+  }
+  acc += __shfl_xor(acc, 8);
+  acc += __shfl_xor(acc, 4);
+  acc += __shfl_xor(acc, 2);
+  acc += __shfl_xor(acc, 1);
+  if (row < rows && sub == 0) Dout[row] = acc;
+}
+
+// ---------------------------------------------------------------- main kernel
+
+template <int D>
+struct BwdCfg {
+  static constexpr int NW = 4;
+  static constexpr int BKV = 32 * NW;               // keys per workgroup
+  static constexpr int BQ = 64;                     // query rows per block
+  static constexpr int QSTR = D + 8;                // row-major Q / dO tile stride
+  static constexpr int TSTR = BQ + 8;               // transposed Q / dO tile stride
+  static constexpr int KTSTR = BKV + 8;             // K^T tile stride
+  static constexpr int DSSTR = BKV + 8;             // dS tile stride
+  static constexpr int UQ = BQ * D / 8 / 256;       // query rows per thread in a tile load
+  static constexpr int NQG = BQ / UQ;
+  static constexpr int UK = BKV * D / 8 / 256;      // key rows per thread in the K^T store
+  static constexpr int NKG = BKV / UK;
+  static_assert(NQG * (D / 8) == 256 && NKG * (D / 8) == 256, "one pass per tile");
+  static constexpr size_t LDS_BYTES =
+      2 * (2 * BQ * QSTR + 2 * D * TSTR) + 2 * D * KTSTR + 2 * BQ * DSSTR + 8 * BQ;
+};
+
+template <int D>
+__global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
+    const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
+    const u16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dg,
+    float* __restrict__ dQ, float* __restrict__ dK, float* __restrict__ dV, int H, int N,
+    float scale, float sl2, int causal, const int32_t* __restrict__ kv_len, int nkb, int total) {
+  using C = BwdCfg<D>;
+  constexpr int BQ = C::BQ;
+  __shared__ __attribute__((aligned(16))) u16 Qs[BQ * C::QSTR];
+  __shared__ __attribute__((aligned(16))) u16 dOs[BQ * C::QSTR];
+  __shared__ __attribute__((aligned(16))) u16 QT[D * C::TSTR];
+  __shared__ __attribute__((aligned(16))) u16 dOT[D * C::TSTR];
+  __shared__ __attribute__((aligned(16))) u16 KT[D * C::KTSTR];
+  __shared__ __attribute__((aligned(16))) u16 dSs[BQ * C::DSSTR];
+  __shared__ __attribute__((aligned(16))) float lse2s[BQ];
+  __shared__ __attribute__((aligned(16))) float Ds[BQ];
+
+  const int tile = xcd_tile(blockIdx.x, total);
+  const int kbi = tile % nkb;  // ascending: causal key blocks with the most rows first
+  const int bh = tile / nkb;
+  const int b = bh / H;
+  const int kb0 = kbi * C::BKV;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, r = lane & 31, g = lane >> 5;
+  const int kw0 = kb0 + 32 * w;
+  const int key = kw0 + r;  // this lane's key (column of S, dP, dV^T, dK^T)
+  const size_t head = (size_t)bh * N * D;
+
+  int kv_lim = N;
+  if (kv_len) {
+    const int L = kv_len[b];
+    kv_lim = L < 0 ? 0 : (L > N ? N : L);
+  }
+
+  f32x16 dv[D / 32], dk[D / 32];
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      dv[t][e] = 0.f;
+      dk[t][e] = 0.f;
+    }
+
+  if (kb0 < kv_lim) {
+    // K and V rows of this lane's key as B operands (column = key, k = d).
+    bf16x8 kf[D / 16], vf[D / 16];
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      u32x4 a = {0u, 0u, 0u, 0u}, c = {0u, 0u, 0u, 0u};
+      if (key < N) {
+        a = ld_global16(K + head + (size_t)key * D + 16 * kk + 8 * g);
+        c = ld_global16(V + head + (size_t)key * D + 16 * kk + 8 * g);
+      }
+      kf[kk] = as_bf16x8(a);
+      vf[kk] = as_bf16x8(c);
+    }
+    // K^T tile of the workgroup's keys, for the dQ product's B operand.
+    {
+      const int kg = tid % C::NKG, dc = tid / C::NKG;
+      u32x4 kr[C::UK];
+#pragma unroll
+      for (int rr = 0; rr < C::UK; ++rr) {
+        const int kk = kb0 + kg * C::UK + rr;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (kk < N) v = ld_global16(K + head + (size_t)kk * D + dc * 8);
+        kr[rr] = v;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        u16* dst = &KT[(dc * 8 + e) * C::KTSTR + kg * C::UK];
+#pragma unroll
+        for (int rr = 0; rr < C::UK; rr += 2)
+          *reinterpret_cast<unsigned*>(dst + rr) = bf16_bits(kr[rr], e) | (bf16_bits(kr[rr + 1], e) << 16);
+      }
+    }
+
+    const int nqb = (N + BQ - 1) / BQ;
+    const int qb_start = causal ? kb0 / BQ : 0;
+    const int qg = tid % C::NQG, qdc = tid / C::NQG;
+    u32x4 qreg[C::UQ], oreg[C::UQ];
+    float lse_reg = 0.f, d_reg = 0.f;
+
+    auto load_q = [&](int q0) {
+#pragma unroll
+      for (int rr = 0; rr < C::UQ; ++rr) {
+        const int qq = q0 + qg * C::UQ + rr;
+        u32x4 a = {0u, 0u, 0u, 0u}, c = {0u, 0u, 0u, 0u};
+        if (qq < N) {
+          a = ld_global16(Q + head + (size_t)qq * D + qdc * 8);
+          c = ld_global16(dO + head + (size_t)qq * D + qdc * 8);
+        }
+        qreg[rr] = a;
+        oreg[rr] = c;
+      }
+      if (tid < BQ) {
+        const int qq = q0 + tid;
+        lse_reg = qq < N ? LSE[(size_t)bh * N + qq] * kLog2e : INFINITY;
+        d_reg = qq < N ? Dg[(size_t)bh * N + qq] : 0.f;
+      }
+    };
+    auto store_q = [&]() {
+#pragma unroll
+      for (int rr = 0; rr < C::UQ; ++rr) {
+        const int row = qg * C::UQ + rr;
+        *reinterpret_cast<u32x4*>(&Qs[row * C::QSTR + qdc * 8]) = qreg[rr];
+        *reinterpret_cast<u32x4*>(&dOs[row * C::QSTR + qdc * 8]) = oreg[rr];
+      }
+      const int col = swap23(qg * C::UQ);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        u16* dq_ = &QT[(qdc * 8 + e) * C::TSTR + col];
+        u16* do_ = &dOT[(qdc * 8 + e) * C::TSTR + col];
+        if constexpr (C::UQ == 4) {
+          u32x2 a, c;
+          a[0] = bf16_bits(qreg[0], e) | (bf16_bits(qreg[1], e) << 16);
+          a[1] = bf16_bits(qreg[2], e) | (bf16_bits(qreg[3], e) << 16);
+          c[0] = bf16_bits(oreg[0], e) | (bf16_bits(oreg[1], e) << 16);
+          c[1] = bf16_bits(oreg[2], e) | (bf16_bits(oreg[3], e) << 16);
+          *reinterpret_cast<u32x2*>(dq_) = a;
+          *reinterpret_cast<u32x2*>(do_) = c;
+        } else {
+          *reinterpret_cast<unsigned*>(dq_) = bf16_bits(qreg[0], e) | (bf16_bits(qreg[1], e) << 16);
+          *reinterpret_cast<unsigned*>(do_) = bf16_bits(oreg[0], e) | (bf16_bits(oreg[1], e) << 16);
+        }
+      }
+      if (tid < BQ) {
+        lse2s[tid] = lse_reg;
+        Ds[tid] = d_reg;
+      }
+    };
+
+    load_q(qb_start * BQ);
+    for (int qb = qb_start; qb < nqb; ++qb) {
+      const int q0 = qb * BQ;
+      store_q();
+      __syncthreads();
+      if (qb + 1 < nqb) load_q(q0 + BQ);
+
+      const bool active = (kw0 < kv_lim) && (!causal || q0 + BQ - 1 >= kw0);
+      if (active) {
+        // S = Q K^T and dP = dO V^T: rows = queries 32*qt + 8i + 4g + j, column = key.
+        f32x16 sa[BQ / 32], pa[BQ / 32];
+#pragma unroll
+        for (int qt = 0; qt < BQ / 32; ++qt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            sa[qt][e] = 0.f;
+            pa[qt][e] = 0.f;
+          }
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+          for (int qt = 0; qt < BQ / 32; ++qt) {
+            sa[qt] = mfma32(ld_lds16(&Qs[(32 * qt + r) * C::QSTR + 16 * kk + 8 * g]), kf[kk], sa[qt]);
+            pa[qt] = mfma32(ld_lds16(&dOs[(32 * qt + r) * C::QSTR + 16 * kk + 8 * g]), vf[kk], pa[qt]);
+          }
+
+        const bool need_mask = (kw0 + 31 >= kv_lim) || (causal && q0 < kw0 + 31);
+#pragma unroll
+        for (int qt = 0; qt < BQ / 32; ++qt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int ql = 32 * qt + 8 * (e >> 2) + 4 * g + (e & 3);
+            float p = fast_exp2(sa[qt][e] * sl2 - lse2s[ql]);
+            if (need_mask && (key >= kv_lim || (causal && key > q0 + ql))) p = 0.f;
+            sa[qt][e] = p;
+            pa[qt][e] = p * (pa[qt][e] - Ds[ql]);
+          }
+
+        bf16x8 pb[BQ / 16], db[BQ / 16];
+#pragma unroll
+        for (int c = 0; c < BQ / 16; ++c) {
+          pb[c] = pack_bf16x8(sa[c >> 1], 8 * (c & 1));
+          db[c] = pack_bf16x8(pa[c >> 1], 8 * (c & 1));
+        }
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+          for (int c = 0; c < BQ / 16; ++c) {
+            dv[t] = mfma32(ld_lds16(&dOT[(32 * t + r) * C::TSTR + 16 * c + 8 * g]), pb[c], dv[t]);
+            dk[t] = mfma32(ld_lds16(&QT[(32 * t + r) * C::TSTR + 16 * c + 8 * g]), db[c], dk[t]);
+          }
+        // dS (bf16) into the row-major [query][key] tile for the dQ product.
+#pragma unroll
+        for (int c = 0; c < BQ / 16; ++c) {
+          const u32x4 words = __builtin_bit_cast(u32x4, db[c]);
+#pragma unroll
+          for (int s8 = 0; s8 < 8; ++s8) {
+            const int ql = 16 * c + 8 * (s8 >> 2) + 4 * g + (s8 & 3);
+            dSs[ql * C::DSSTR + 32 * w + r] = (u16)(words[s8 >> 1] >> ((s8 & 1) * 16));
+          }
+        }
+      } else {
+        for (int idx = lane; idx < BQ * 4; idx += 64) {
+          const u32x4 z = {0u, 0u, 0u, 0u};
+          *reinterpret_cast<u32x4*>(&dSs[(idx >> 2) * C::DSSTR + 32 * w + 8 * (idx & 3)]) = z;
+        }
+      }
+      __syncthreads();
+
+      // dQ_i += s dS K over the workgroup's keys: tiles (qt, dt) of 32 x 32, split over waves.
+      constexpr int NT = (BQ / 32) * (D / 32);
+      for (int tt = w; tt < NT; tt += C::NW) {
+        const int qt = tt / (D / 32), dt = tt % (D / 32);
+        f32x16 acc;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+#pragma unroll
+        for (int c = 0; c < C::BKV / 16; ++c)
+          acc = mfma32(ld_lds16(&dSs[(32 * qt + r) * C::DSSTR + 16 * c + 8 * g]),
+                       ld_lds16(&KT[(32 * dt + r) * C::KTSTR + 16 * c + 8 * g]), acc);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int qq = q0 + 32 * qt + 8 * (e >> 2) + 4 * g + (e & 3);
+          if (qq < N) unsafeAtomicAdd(dQ + head + (size_t)qq * D + 32 * dt + r, acc[e] * scale);
+        }
+      }
+    }
+  }
+
+  if (key < N) {
+    float* dkrow = dK + head + (size_t)key * D;
+    float* dvrow = dV + head + (size_t)key * D;
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f32x4 a, c;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          a[j] = dk[t][4 * i + j] * scale;
+          c[j] = dv[t][4 * i + j];
+        }
+        *reinterpret_cast<f32x4*>(dkrow + 32 * t + 8 * i + 4 * g) = a;
+        *reinterpret_cast<f32x4*>(dvrow + 32 * t + 8 * i + 4 * g) = c;
+      }
+  }
+}
+
+template <int D>
+static hipError_t launch_bwd_d(const void* Q, const void* K, const void* V, const void* O,
+                               const void* dO, const float* LSE, float* dQ, float* dK, float* dV,
+                               float* Dws, const AttnShape& s, bool precise, hipStream_t stream) {
+  (void)precise;
+  const size_t rows = (size_t)s.B * s.H * s.N;
+  hipError_t e = fill_zero(dQ, rows * D, stream);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_dot_kernel<D>, dim3((unsigned)((rows * 16 + 255) / 256)), dim3(256), 0, stream,
+                     static_cast<const u16*>(O), static_cast<const u16*>(dO), Dws, (int)rows);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nkb = (s.N + BwdCfg<D>::BKV - 1) / BwdCfg<D>::BKV;
+  const int total = s.B * s.H * nkb;
+  hipLaunchKernelGGL(bwd_bf16_kernel<D>, dim3(total), dim3(256), 0, stream,
+                     static_cast<const u16*>(Q), static_cast<const u16*>(K),
+                     static_cast<const u16*>(V), static_cast<const u16*>(dO), LSE, Dws, dQ, dK, dV,
+                     s.H, s.N, s.scale, s.scale * kLog2e, s.causal, s.kv_len, nkb, total);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_bf16(const void* Q, const void* K, const void* V, const void* O,
+                           const void* dO, const float* LSE, float* dQ, float* dK, float* dV,
+                           float* Dws, const AttnShape& s, bool precise, hipStream_t stream) {
+  if (s.d == 64) return launch_bwd_d<64>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, s, precise, stream);
+  return launch_bwd_d<128>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, s, precise, stream);
+}
+
+}  // namespace fa

@@ -1,0 +1,159 @@
+// extern "C" entry points of libflashattn.so: argument checks on the host,
+// then dispatch to the gfx950 launchers. Nothing is enqueued unless every
+// check passes.
+#include "../../include/flash_attn.h"
+
+#include <math.h>
+#include <stdint.h>
+
+#include "fa_launch.h"
+
+namespace {
+
+struct Span {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Span span(const void* p, size_t bytes) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Span{a, a + bytes};
+}
+
+bool overlaps(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shape, scale and flag checks common to every entry point.
+int check_shape(int B, int H, int N, int d, float scale) {
+  if (B < 1 || H < 1 || N < 1 || d < 1) return FA_ERR_INVALID_ARG;
+  if (!isfinite(scale) || !(scale > 0.f)) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  const int64_t elems = (int64_t)B * H * N * d;
+  if (elems > INT32_MAX) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
+// Pointer checks: non-NULL, 16-byte aligned, and no output overlapping any
+// other tensor (inputs or outputs).
+int check_ptrs(const Span* in, const void* const* in_p, int n_in, const Span* out,
+               const void* const* out_p, int n_out) {
+  for (int i = 0; i < n_in; ++i)
+    if (!in_p[i] || !aligned16(in_p[i])) return FA_ERR_INVALID_ARG;
+  for (int i = 0; i < n_out; ++i)
+    if (!out_p[i] || !aligned16(out_p[i])) return FA_ERR_INVALID_ARG;
+  for (int i = 0; i < n_out; ++i) {
+    for (int j = 0; j < n_in; ++j)
+      if (overlaps(out[i], in[j])) return FA_ERR_INVALID_ARG;
+    for (int j = i + 1; j < n_out; ++j)
+      if (overlaps(out[i], out[j])) return FA_ERR_INVALID_ARG;
+  }
+  return FA_OK;
+}
+
+size_t workspace_bytes(int B, int H, int N) {
+  const size_t rows = (size_t)B * H * N;
+  return (rows * sizeof(float) + 255) & ~(size_t)255;
+}
+
+int fwd_common(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H, int N,
+               int d, float scale, int causal, size_t esize) {
+  int st = check_shape(B, H, N, d, scale);
+  if (st != FA_OK) return st;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  const size_t tbytes = (size_t)B * H * N * d * esize;
+  const size_t lbytes = (size_t)B * H * N * sizeof(float);
+  const void* in_p[3] = {Q, K, V};
+  const Span in[3] = {span(Q, tbytes), span(K, tbytes), span(V, tbytes)};
+  const void* out_p[2] = {O, LSE};
+  const Span out[2] = {span(O, tbytes), span(LSE, lbytes)};
+  return check_ptrs(in, in_p, 3, out, out_p, 2);
+}
+
+int bwd_common(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+               const float* LSE, float* dQ, float* dK, float* dV, void* ws, size_t ws_bytes, int B,
+               int H, int N, int d, float scale, int causal, unsigned flags, unsigned allowed_flags,
+               size_t esize) {
+  int st = check_shape(B, H, N, d, scale);
+  if (st != FA_OK) return st;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  if (flags & ~allowed_flags) return FA_ERR_INVALID_ARG;
+  const size_t need = workspace_bytes(B, H, N);
+  if (ws_bytes < need) return FA_ERR_INVALID_ARG;
+  const size_t tbytes = (size_t)B * H * N * d * esize;
+  const size_t gbytes = (size_t)B * H * N * d * sizeof(float);
+  const size_t lbytes = (size_t)B * H * N * sizeof(float);
+  const void* in_p[6] = {Q, K, V, O, dO, LSE};
+  const Span in[6] = {span(Q, tbytes), span(K, tbytes), span(V, tbytes),
+                      span(O, tbytes), span(dO, tbytes), span(LSE, lbytes)};
+  const void* out_p[4] = {dQ, dK, dV, ws};
+  const Span out[4] = {span(dQ, gbytes), span(dK, gbytes), span(dV, gbytes), span(ws, need)};
+  return check_ptrs(in, in_p, 6, out, out_p, 4);
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int flash_attn_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
+                   int N, int d, float scale, int causal, const int32_t* kv_len, void* stream) {
+  const int st = fwd_common(Q, K, V, O, LSE, B, H, N, d, scale, causal, 2);
+  if (st != FA_OK) return st;
+  const fa::AttnShape s{B, H, N, d, scale, causal, kv_len};
+  return hip_status(fa::launch_fwd_bf16(Q, K, V, O, LSE, s, static_cast<hipStream_t>(stream)));
+}
+
+int flash_attn_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                   const float* LSE, float* dQ, float* dK, float* dV, void* workspace,
+                   size_t workspace_bytes_, int B, int H, int N, int d, float scale, int causal,
+                   const int32_t* kv_len, unsigned flags, void* stream) {
+  const int st = bwd_common(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, workspace_bytes_, B, H, N, d,
+                            scale, causal, flags, FA_BWD_PRECISE, 2);
+  if (st != FA_OK) return st;
+  if (flags & FA_BWD_PRECISE) return FA_ERR_UNSUPPORTED;
+  const fa::AttnShape s{B, H, N, d, scale, causal, kv_len};
+  return hip_status(fa::launch_bwd_bf16(Q, K, V, O, dO, LSE, dQ, dK, dV, static_cast<float*>(workspace),
+                                        s, (flags & FA_BWD_PRECISE) != 0,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+size_t flash_attn_bwd_workspace_bytes(int B, int H, int N, int d, unsigned flags) {
+  (void)flags;
+  if (B < 1 || H < 1 || N < 1 || d < 1) return 0;
+  return workspace_bytes(B, H, N);
+}
+
+int flash_attn_fwd_f32(const float* Q, const float* K, const float* V, float* O, float* LSE, int B,
+                       int H, int N, int d, float scale, int causal, const int32_t* kv_len,
+                       void* stream) {
+  const int st = fwd_common(Q, K, V, O, LSE, B, H, N, d, scale, causal, 4);
+  if (st != FA_OK) return st;
+  const fa::AttnShape s{B, H, N, d, scale, causal, kv_len};
+  return hip_status(fa::launch_fwd_f32(Q, K, V, O, LSE, s, static_cast<hipStream_t>(stream)));
+}
+
+int flash_attn_bwd_f32(const float* Q, const float* K, const float* V, const float* O,
+                       const float* dO, const float* LSE, float* dQ, float* dK, float* dV,
+                       void* workspace, size_t workspace_bytes_, int B, int H, int N, int d,
+                       float scale, int causal, const int32_t* kv_len, unsigned flags,
+                       void* stream) {
+  const int st = bwd_common(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, workspace_bytes_, B, H, N, d,
+                            scale, causal, flags, 0u, 4);
+  if (st != FA_OK) return st;
+  const fa::AttnShape s{B, H, N, d, scale, causal, kv_len};
+  return hip_status(fa::launch_bwd_f32(Q, K, V, O, dO, LSE, dQ, dK, dV, static_cast<float*>(workspace),
+                                       s, static_cast<hipStream_t>(stream)));
+}
+
+const char* flash_attn_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG: an argument failed the host-side checks";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: request is well-formed but not implemented";
+    case FA_ERR_HIP: return "FA_ERR_HIP: a kernel launch failed";
+    default: return "unknown flash_attn status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,121 @@
+"""The C ABI: exported symbols and host-side argument checks (CPU only).
+
+Every call below fails a host check, so it returns before anything touches a
+GPU; none of them computes.
+"""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import io_aware_exact_11_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flash_attn.h")
+
+FAKE = 0x10000  # a 16-byte-aligned address that is never dereferenced
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(flash_attn_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return fa.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert set(names) == set(fa.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for st in range(4):
+        assert fa.flash_attn_status_string(st).startswith(["FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_HIP"][st])
+    assert "unknown" in fa.flash_attn_status_string(99)
+
+
+def test_workspace_bytes(lib):
+    assert fa.flash_attn_bwd_workspace_bytes(2, 3, 100, 64) == ((2 * 3 * 100 * 4 + 255) // 256) * 256
+    assert fa.flash_attn_bwd_workspace_bytes(0, 3, 100, 64) == 0
+    assert fa.flash_attn_bwd_workspace_bytes(1, 1, 1, 128) == 256
+
+
+def _fwd(lib, B=1, H=1, N=16, d=64, scale=0.125, causal=0, ptrs=None, fn="flash_attn_fwd", esize=2):
+    span = B * H * N * d * esize + 4096
+    base = [FAKE + i * ((span + 4095) // 4096 * 4096) for i in range(5)]
+    if ptrs:
+        base = [ptrs.get(i, b) for i, b in enumerate(base)]
+    return getattr(lib, fn)(*[ctypes.c_void_p(p) if p is not None else None for p in base],
+                            B, H, N, d, scale, causal, None, None)
+
+
+def _bwd(lib, B=1, H=1, N=16, d=64, scale=0.125, causal=0, flags=0, ws=None, ptrs=None,
+         fn="flash_attn_bwd", esize=4):
+    span = B * H * N * d * max(esize, 4) + 4096
+    step = (span + 4095) // 4096 * 4096
+    base = [FAKE + i * step for i in range(10)]
+    if ptrs:
+        base = [ptrs.get(i, b) for i, b in enumerate(base)]
+    wsb = fa.flash_attn_bwd_workspace_bytes(B, H, N, d, flags) if ws is None else ws
+    args = [ctypes.c_void_p(p) if p is not None else None for p in base]
+    return getattr(lib, fn)(*args, wsb, B, H, N, d, scale, causal, None, flags, None)
+
+
+@pytest.mark.parametrize("fn,esize", [("flash_attn_fwd", 2), ("flash_attn_fwd_f32", 4)])
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), fa.binding.FA_ERR_INVALID_ARG),
+    (dict(H=-1), fa.binding.FA_ERR_INVALID_ARG),
+    (dict(N=0), fa.binding.FA_ERR_INVALID_ARG),
+    (dict(d=0), fa.binding.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.binding.FA_ERR_UNSUPPORTED),
+    (dict(d=256), fa.binding.FA_ERR_UNSUPPORTED),
+    (dict(scale=0.0), fa.binding.FA_ERR_INVALID_ARG),
+    (dict(scale=-1.0), fa.binding.FA_ERR_INVALID_ARG),
+    (dict(scale=math.nan), fa.binding.FA_ERR_INVALID_ARG),
+    (dict(scale=math.inf), fa.binding.FA_ERR_INVALID_ARG),
+    (dict(causal=2), fa.binding.FA_ERR_INVALID_ARG),
+    (dict(B=4096, H=64, N=8192, d=128), fa.binding.FA_ERR_UNSUPPORTED),
+    (dict(ptrs={0: None}), fa.binding.FA_ERR_INVALID_ARG),
+    (dict(ptrs={2: None}), fa.binding.FA_ERR_INVALID_ARG),
+    (dict(ptrs={4: None}), fa.binding.FA_ERR_INVALID_ARG),
+    (dict(ptrs={1: FAKE + 8}), fa.binding.FA_ERR_INVALID_ARG),
+    (dict(ptrs={3: FAKE}), fa.binding.FA_ERR_INVALID_ARG),          # O aliases Q
+    (dict(ptrs={4: FAKE + 64}), fa.binding.FA_ERR_INVALID_ARG),     # LSE inside Q
+])
+def test_fwd_rejects(lib, fn, esize, kw, status):
+    assert _fwd(lib, fn=fn, esize=esize, **kw) == status
+
+
+@pytest.mark.parametrize("fn", ["flash_attn_bwd", "flash_attn_bwd_f32"])
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), fa.binding.FA_ERR_INVALID_ARG),
+    (dict(d=80), fa.binding.FA_ERR_UNSUPPORTED),
+    (dict(scale=math.nan), fa.binding.FA_ERR_INVALID_ARG),
+    (dict(flags=1 << 5), fa.binding.FA_ERR_INVALID_ARG),
+    (dict(ws=16), fa.binding.FA_ERR_INVALID_ARG),
+    (dict(ptrs={9: None}), fa.binding.FA_ERR_INVALID_ARG),          # NULL workspace
+    (dict(ptrs={5: None}), fa.binding.FA_ERR_INVALID_ARG),          # NULL LSE
+    (dict(ptrs={6: FAKE}), fa.binding.FA_ERR_INVALID_ARG),          # dQ aliases Q
+    (dict(ptrs={7: FAKE + 6 * 8192}), fa.binding.FA_ERR_INVALID_ARG),   # dK aliases dQ (8192-byte slots)
+    (dict(ptrs={8: FAKE + 4}), fa.binding.FA_ERR_INVALID_ARG),      # misaligned dV
+])
+def test_bwd_rejects(lib, fn, kw, status):
+    assert _bwd(lib, fn=fn, **kw) == status
+
+
+def test_f32_bwd_rejects_precise_flag(lib):
+    assert _bwd(lib, fn="flash_attn_bwd_f32", flags=fa.FA_BWD_PRECISE) == fa.binding.FA_ERR_INVALID_ARG
+
+
+def test_binding_fails_loudly_without_gpu_tensors():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.flash_attn_fwd(x, x, x)
