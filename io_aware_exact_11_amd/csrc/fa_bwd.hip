@@ -79,6 +79,134 @@ __global__ __launch_bounds__(256) void bwd_dot_kernel(const u16* __restrict__ O,
   if (row < rows && sub == 0) Dout[row] = acc;
 }
 
+// D_i = sum_j P_ij dP_ij taken literally, for FA_BWD_PRECISE: a query-outer
+// pass (one workgroup per 128 query rows, 32 per wave) that recomputes the
+// score tile S^T = K Q^T and dP^T = V dO^T on the matrix cores, with both K
+// and V tiles streamed row-major through double-buffered LDS and the wave's
+// Q and dO rows held as B operands; P_ij = 2^(s_ij*scale*log2e - LSE_i*log2e)
+// uses the saved LSE. Independent of O, so the bf16 rounding of O does not
+// enter D.
+template <int D>
+struct ExactDCfg {
+  static constexpr int BR = 128;
+  static constexpr int BC = 64;
+  static constexpr int KSTR = D + 8;
+  static constexpr int KCH = BC * D / 8 / 256;
+};
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void bwd_exact_d_kernel(
+    const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
+    const u16* __restrict__ dO, const float* __restrict__ LSE, float* __restrict__ Dout, int H,
+    int N, float sl2, int causal, const int32_t* __restrict__ kv_len, int nqb, int total) {
+  using C = ExactDCfg<D>;
+  constexpr int BC = C::BC;
+  __shared__ __attribute__((aligned(16))) u16 Ks[2][BC * C::KSTR];
+  __shared__ __attribute__((aligned(16))) u16 Vs[2][BC * C::KSTR];
+
+  const int tile = xcd_tile(blockIdx.x, total);
+  int qb = tile % nqb;
+  const int bh = tile / nqb;
+  if (causal) qb = nqb - 1 - qb;
+  const int b = bh / H;
+  const int q0 = qb * C::BR;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, r = lane & 31, g = lane >> 5;
+  const size_t head = (size_t)bh * N * D;
+
+  int kv_lim = N;
+  if (kv_len) {
+    const int L = kv_len[b];
+    kv_lim = L < 0 ? 0 : (L > N ? N : L);
+  }
+  int kv_end = kv_lim;
+  if (causal) kv_end = min(kv_end, q0 + C::BR);
+  const int nt = (kv_end + BC - 1) / BC;
+
+  const int q = q0 + 32 * w + r;
+  const int wave_q_first = q0 + 32 * w, wave_q_last = wave_q_first + 31;
+  bf16x8 qf[D / 16], df[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    u32x4 a = {0u, 0u, 0u, 0u}, c = {0u, 0u, 0u, 0u};
+    if (q < N) {
+      a = ld_global16(Q + head + (size_t)q * D + 16 * kk + 8 * g);
+      c = ld_global16(dO + head + (size_t)q * D + 16 * kk + 8 * g);
+    }
+    qf[kk] = as_bf16x8(a);
+    df[kk] = as_bf16x8(c);
+  }
+  const float lse2 = q < N ? LSE[(size_t)bh * N + q] * kLog2e : INFINITY;
+  float part = 0.f;
+
+  u32x4 kreg[C::KCH], vreg[C::KCH];
+  auto load_tile = [&](int kb) {
+#pragma unroll
+    for (int rr = 0; rr < C::KCH; ++rr) {
+      const int c = tid + 256 * rr;
+      const int key = kb + c / (D / 8);
+      u32x4 a = {0u, 0u, 0u, 0u}, v = {0u, 0u, 0u, 0u};
+      if (key < N) {
+        a = ld_global16(K + head + (size_t)key * D + (c % (D / 8)) * 8);
+        v = ld_global16(V + head + (size_t)key * D + (c % (D / 8)) * 8);
+      }
+      kreg[rr] = a;
+      vreg[rr] = v;
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int rr = 0; rr < C::KCH; ++rr) {
+      const int c = tid + 256 * rr;
+      const int off = (c / (D / 8)) * C::KSTR + (c % (D / 8)) * 8;
+      *reinterpret_cast<u32x4*>(&Ks[buf][off]) = kreg[rr];
+      *reinterpret_cast<u32x4*>(&Vs[buf][off]) = vreg[rr];
+    }
+  };
+
+  if (nt > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+  for (int it = 0; it < nt; ++it) {
+    const int buf = it & 1;
+    const int kb = it * BC;
+    if (it + 1 < nt) load_tile(kb + BC);
+    if (!causal || kb <= wave_q_last) {
+      f32x16 s[BC / 32], dp[BC / 32];
+#pragma unroll
+      for (int mt = 0; mt < BC / 32; ++mt) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          s[mt][e] = 0.f;
+          dp[mt][e] = 0.f;
+        }
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+          const int off = (32 * mt + r) * C::KSTR + 16 * kk + 8 * g;
+          s[mt] = mfma32(ld_lds16(&Ks[buf][off]), qf[kk], s[mt]);
+          dp[mt] = mfma32(ld_lds16(&Vs[buf][off]), df[kk], dp[mt]);
+        }
+      }
+      const bool need_mask = (kb + BC > kv_lim) || (causal && kb + BC - 1 > wave_q_first);
+#pragma unroll
+      for (int mt = 0; mt < BC / 32; ++mt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = kb + 32 * mt + 8 * (e >> 2) + 4 * g + (e & 3);
+          float p = fast_exp2(s[mt][e] * sl2 - lse2);
+          if (need_mask && (key >= kv_lim || (causal && key > q))) p = 0.f;
+          part += p * dp[mt][e];
+        }
+    }
+    if (it + 1 < nt) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+  part += __shfl_xor(part, 32);
+  if (q < N && g == 0) Dout[(size_t)bh * N + q] = part;
+}
+
 // ---------------------------------------------------------------- main kernel
 
 template <int D>
@@ -99,7 +227,7 @@ struct BwdCfg {
       2 * (2 * BQ * QSTR + 2 * D * TSTR) + 2 * D * KTSTR + 2 * BQ * DSSTR + 8 * BQ;
 };
 
-template <int D>
+template <int D, bool PRECISE>
 __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
     const u16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dg,
@@ -112,7 +240,8 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
   __shared__ __attribute__((aligned(16))) u16 QT[D * C::TSTR];
   __shared__ __attribute__((aligned(16))) u16 dOT[D * C::TSTR];
   __shared__ __attribute__((aligned(16))) u16 KT[D * C::KTSTR];
-  __shared__ __attribute__((aligned(16))) u16 dSs[BQ * C::DSSTR];
+  // dS tile; in precise mode followed by the low half of its bf16 split.
+  __shared__ __attribute__((aligned(16))) u16 dSs[(PRECISE ? 2 : 1) * BQ * C::DSSTR];
   __shared__ __attribute__((aligned(16))) float lse2s[BQ];
   __shared__ __attribute__((aligned(16))) float Ds[BQ];
 
@@ -268,31 +397,46 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
             pa[qt][e] = p * (pa[qt][e] - Ds[ql]);
           }
 
-        bf16x8 pb[BQ / 16], db[BQ / 16];
+        bf16x8 pb[BQ / 16], db[BQ / 16], pl[PRECISE ? BQ / 16 : 1], dl[PRECISE ? BQ / 16 : 1];
 #pragma unroll
         for (int c = 0; c < BQ / 16; ++c) {
-          pb[c] = pack_bf16x8(sa[c >> 1], 8 * (c & 1));
-          db[c] = pack_bf16x8(pa[c >> 1], 8 * (c & 1));
+          if constexpr (PRECISE) {
+            pack_split_bf16x8(sa[c >> 1], 8 * (c & 1), pb[c], pl[c]);
+            pack_split_bf16x8(pa[c >> 1], 8 * (c & 1), db[c], dl[c]);
+          } else {
+            pb[c] = pack_bf16x8(sa[c >> 1], 8 * (c & 1));
+            db[c] = pack_bf16x8(pa[c >> 1], 8 * (c & 1));
+          }
         }
 #pragma unroll
         for (int t = 0; t < D / 32; ++t)
 #pragma unroll
           for (int c = 0; c < BQ / 16; ++c) {
-            dv[t] = mfma32(ld_lds16(&dOT[(32 * t + r) * C::TSTR + 16 * c + 8 * g]), pb[c], dv[t]);
-            dk[t] = mfma32(ld_lds16(&QT[(32 * t + r) * C::TSTR + 16 * c + 8 * g]), db[c], dk[t]);
+            const bf16x8 aO = ld_lds16(&dOT[(32 * t + r) * C::TSTR + 16 * c + 8 * g]);
+            const bf16x8 aQ = ld_lds16(&QT[(32 * t + r) * C::TSTR + 16 * c + 8 * g]);
+            dv[t] = mfma32(aO, pb[c], dv[t]);
+            dk[t] = mfma32(aQ, db[c], dk[t]);
+            if constexpr (PRECISE) {
+              dv[t] = mfma32(aO, pl[c], dv[t]);
+              dk[t] = mfma32(aQ, dl[c], dk[t]);
+            }
           }
         // dS (bf16) into the row-major [query][key] tile for the dQ product.
 #pragma unroll
-        for (int c = 0; c < BQ / 16; ++c) {
-          const u32x4 words = __builtin_bit_cast(u32x4, db[c]);
+        for (int part = 0; part < (PRECISE ? 2 : 1); ++part) {
+          u16* dst = dSs + part * BQ * C::DSSTR;
 #pragma unroll
-          for (int s8 = 0; s8 < 8; ++s8) {
-            const int ql = 16 * c + 8 * (s8 >> 2) + 4 * g + (s8 & 3);
-            dSs[ql * C::DSSTR + 32 * w + r] = (u16)(words[s8 >> 1] >> ((s8 & 1) * 16));
+          for (int c = 0; c < BQ / 16; ++c) {
+            const u32x4 words = __builtin_bit_cast(u32x4, part == 0 ? db[c] : dl[PRECISE ? c : 0]);
+#pragma unroll
+            for (int s8 = 0; s8 < 8; ++s8) {
+              const int ql = 16 * c + 8 * (s8 >> 2) + 4 * g + (s8 & 3);
+              dst[ql * C::DSSTR + 32 * w + r] = (u16)(words[s8 >> 1] >> ((s8 & 1) * 16));
+            }
           }
         }
       } else {
-        for (int idx = lane; idx < BQ * 4; idx += 64) {
+        for (int idx = lane; idx < (PRECISE ? 2 : 1) * BQ * 4; idx += 64) {
           const u32x4 z = {0u, 0u, 0u, 0u};
           *reinterpret_cast<u32x4*>(&dSs[(idx >> 2) * C::DSSTR + 32 * w + 8 * (idx & 3)]) = z;
         }
@@ -307,9 +451,12 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[e] = 0.f;
 #pragma unroll
-        for (int c = 0; c < C::BKV / 16; ++c)
-          acc = mfma32(ld_lds16(&dSs[(32 * qt + r) * C::DSSTR + 16 * c + 8 * g]),
-                       ld_lds16(&KT[(32 * dt + r) * C::KTSTR + 16 * c + 8 * g]), acc);
+        for (int c = 0; c < C::BKV / 16; ++c) {
+          const bf16x8 bK = ld_lds16(&KT[(32 * dt + r) * C::KTSTR + 16 * c + 8 * g]);
+          acc = mfma32(ld_lds16(&dSs[(32 * qt + r) * C::DSSTR + 16 * c + 8 * g]), bK, acc);
+          if constexpr (PRECISE)
+            acc = mfma32(ld_lds16(&dSs[(BQ + 32 * qt + r) * C::DSSTR + 16 * c + 8 * g]), bK, acc);
+        }
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int qq = q0 + 32 * qt + 8 * (e >> 2) + 4 * g + (e & 3);
@@ -342,20 +489,35 @@ template <int D>
 static hipError_t launch_bwd_d(const void* Q, const void* K, const void* V, const void* O,
                                const void* dO, const float* LSE, float* dQ, float* dK, float* dV,
                                float* Dws, const AttnShape& s, bool precise, hipStream_t stream) {
-  (void)precise;
   const size_t rows = (size_t)s.B * s.H * s.N;
+  const float sl2 = s.scale * kLog2e;
   hipError_t e = fill_zero(dQ, rows * D, stream);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_dot_kernel<D>, dim3((unsigned)((rows * 16 + 255) / 256)), dim3(256), 0, stream,
-                     static_cast<const u16*>(O), static_cast<const u16*>(dO), Dws, (int)rows);
+  if (precise) {
+    const int nqb = (s.N + ExactDCfg<D>::BR - 1) / ExactDCfg<D>::BR;
+    const int total = s.B * s.H * nqb;
+    hipLaunchKernelGGL(bwd_exact_d_kernel<D>, dim3(total), dim3(256), 0, stream,
+                       static_cast<const u16*>(Q), static_cast<const u16*>(K),
+                       static_cast<const u16*>(V), static_cast<const u16*>(dO), LSE, Dws, s.H, s.N,
+                       sl2, s.causal, s.kv_len, nqb, total);
+  } else {
+    hipLaunchKernelGGL(bwd_dot_kernel<D>, dim3((unsigned)((rows * 16 + 255) / 256)), dim3(256), 0,
+                       stream, static_cast<const u16*>(O), static_cast<const u16*>(dO), Dws, (int)rows);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nkb = (s.N + BwdCfg<D>::BKV - 1) / BwdCfg<D>::BKV;
   const int total = s.B * s.H * nkb;
-  hipLaunchKernelGGL(bwd_bf16_kernel<D>, dim3(total), dim3(256), 0, stream,
-                     static_cast<const u16*>(Q), static_cast<const u16*>(K),
-                     static_cast<const u16*>(V), static_cast<const u16*>(dO), LSE, Dws, dQ, dK, dV,
-                     s.H, s.N, s.scale, s.scale * kLog2e, s.causal, s.kv_len, nkb, total);
+  if (precise)
+    hipLaunchKernelGGL((bwd_bf16_kernel<D, true>), dim3(total), dim3(256), 0, stream,
+                       static_cast<const u16*>(Q), static_cast<const u16*>(K),
+                       static_cast<const u16*>(V), static_cast<const u16*>(dO), LSE, Dws, dQ, dK, dV,
+                       s.H, s.N, s.scale, sl2, s.causal, s.kv_len, nkb, total);
+  else
+    hipLaunchKernelGGL((bwd_bf16_kernel<D, false>), dim3(total), dim3(256), 0, stream,
+                       static_cast<const u16*>(Q), static_cast<const u16*>(K),
+                       static_cast<const u16*>(V), static_cast<const u16*>(dO), LSE, Dws, dQ, dK, dV,
+                       s.H, s.N, s.scale, sl2, s.causal, s.kv_len, nkb, total);
   return hipGetLastError();
 }
 

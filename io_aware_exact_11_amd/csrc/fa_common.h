@@ -46,6 +46,18 @@ __device__ __forceinline__ bf16x8 pack_bf16x8(const f32x16& v, int base) {
   return r;
 }
 
+// Split 8 fp32 values into bf16 pairs with x ~ hi + lo: hi = bf16(x),
+// lo = bf16(x - hi). Two products over (hi, lo) carry about 16 significant
+// bits of x instead of 8.
+__device__ __forceinline__ void pack_split_bf16x8(const f32x16& v, int base, bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const __bf16 h = (__bf16)v[base + e];
+    hi[e] = h;
+    lo[e] = (__bf16)(v[base + e] - (float)h);
+  }
+}
+
 // Element e (0..7) of a 16-byte chunk of bf16 values, as raw bits.
 __device__ __forceinline__ unsigned bf16_bits(const u32x4& v, int e) {
   return (v[e >> 1] >> ((e & 1) * 16)) & 0xffffu;

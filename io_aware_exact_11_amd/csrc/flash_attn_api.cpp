@@ -111,7 +111,6 @@ int flash_attn_bwd(const void* Q, const void* K, const void* V, const void* O, c
   const int st = bwd_common(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, workspace_bytes_, B, H, N, d,
                             scale, causal, flags, FA_BWD_PRECISE, 2);
   if (st != FA_OK) return st;
-  if (flags & FA_BWD_PRECISE) return FA_ERR_UNSUPPORTED;
   const fa::AttnShape s{B, H, N, d, scale, causal, kv_len};
   return hip_status(fa::launch_bwd_bf16(Q, K, V, O, dO, LSE, dQ, dK, dV, static_cast<float*>(workspace),
                                         s, (flags & FA_BWD_PRECISE) != 0,
