@@ -1,0 +1,264 @@
+"""Benchmark: one step = exact-attention forward + backward over one batch.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Prints one JSON line. The step runs the library's whole path on inputs that
+are already resident in device memory: flash_attn_fwd (O, LSE) then
+flash_attn_bwd (dQ zero-fill, D pre-pass, main backward kernel). FLOPs are
+counted over visible (query, key) pairs only: 4 d per pair forward (the two
+products S = Q K^T and O = P V at 2 flops per multiply-add) and 10 d per
+pair backward (recomputed S, dP, dV, dK, dQ), 14 d per pair for a step.
+
+The primary workload is the GPT-2-medium attention shape (B=64, H=16,
+N=1024, d=64, causal); the N=4096 and N=16384 head-dim-128 workloads are
+timed the same way and reported under "workloads". Only one GPU is used.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 matrix-core peak (2.5 PFLOP/s class)
+PRIMARY = "gpt2_medium"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def pairs_per_batch(w, causal, kv_len):
+    """Visible (query, key) pairs summed over all heads."""
+    N = w.N
+    if kv_len is not None:
+        tot = 0
+        for L in kv_len:
+            L = max(0, min(int(L), N))
+            tot += (sum(min(i + 1, L) for i in range(N)) if causal else N * L)
+        return tot * w.H
+    per_head = N * (N + 1) // 2 if causal else N * N
+    return per_head * w.B * w.H
+
+
+def kernel_source_digest():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "io_aware_exact_11_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+class Case:
+    """Device-resident inputs and outputs of one workload."""
+
+    def __init__(self, name, causal, precise=False):
+        import torch
+        from io_aware_exact_11_amd import workloads as wl
+        import io_aware_exact_11_amd as fa
+        self.fa = fa
+        self.w = wl.WORKLOADS[name]
+        self.name, self.causal, self.precise = name, causal, precise
+        x = wl.workload_inputs(name)
+        dev = lambda bits: torch.from_numpy(bits.view("int16")).view(torch.bfloat16).cuda()
+        self.q, self.k, self.v, self.do = (dev(x[n + "_bits"]) for n in ("Q", "K", "V", "dO"))
+        self.kv_host = x["kv_len"]
+        self.kv = None if x["kv_len"] is None else torch.from_numpy(x["kv_len"]).cuda()
+        del x
+        w = self.w
+        f32 = dict(dtype=torch.float32, device="cuda")
+        self.o = torch.empty_like(self.q)
+        self.lse = torch.empty((w.B, w.H, w.N), **f32)
+        self.dq = torch.empty((w.B, w.H, w.N, w.d), **f32)
+        self.dk = torch.empty_like(self.dq)
+        self.dv = torch.empty_like(self.dq)
+        self.ws = torch.empty(fa.flash_attn_bwd_workspace_bytes(w.B, w.H, w.N, w.d),
+                              dtype=torch.uint8, device="cuda")
+        self.pairs = pairs_per_batch(w, causal, self.kv_host)
+
+    def fwd(self):
+        self.fa.flash_attn_fwd(self.q, self.k, self.v, causal=self.causal, scale=self.w.scale,
+                               kv_len=self.kv, out=self.o, lse=self.lse)
+
+    def bwd(self):
+        self.fa.flash_attn_bwd(self.q, self.k, self.v, self.o, self.do, self.lse, causal=self.causal,
+                               scale=self.w.scale, kv_len=self.kv, precise=self.precise,
+                               dq=self.dq, dk=self.dk, dv=self.dv, workspace=self.ws)
+
+    def run(self, steps, warmup):
+        """Time `steps` whole steps; per-kernel-call times from events on the stream."""
+        import torch
+        for _ in range(warmup):
+            self.fwd()
+            self.bwd()
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        t0 = time.perf_counter()
+        for e in ev:
+            e[0].record()
+            self.fwd()
+            e[1].record()
+            self.bwd()
+            e[2].record()
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / steps
+        fwd_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+        bwd_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+        return wall * 1e3, fwd_ms, bwd_ms
+
+    def flops(self):
+        d = self.w.d
+        mult_bwd = 14 if self.precise else 10  # precise: exact-D pass (2) and hi/lo products (2)
+        return 4 * d * self.pairs, mult_bwd * d * self.pairs
+
+
+def cpu_baseline(name, causal, budget_s=10.0):
+    """The fp64 oracle timed on this host's cores on a bounded sample of heads
+    of the same workload (its first heads in (b, h) order, until about
+    budget_s of work), reported in the same algorithmic TFLOP/s (14 d per pair)."""
+    import oracle
+    from io_aware_exact_11_amd import workloads as wl
+    w = wl.WORKLOADS[name]
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max(i["num_threads"] for i in threadpool_info())
+    except Exception:
+        threads = os.cpu_count()
+    x = wl.workload_inputs(name)
+    heads, t0 = 0, time.perf_counter()
+    while heads < w.B * w.H and (time.perf_counter() - t0) < budget_s:
+        b, h = divmod(heads, w.H)
+        oracle.head_forward(x["Q"][b, h], x["K"][b, h], x["V"][b, h], w.scale, causal)
+        oracle.head_backward(x["Q"][b, h], x["K"][b, h], x["V"][b, h], x["dO"][b, h], w.scale, causal)
+        heads += 1
+    dt = time.perf_counter() - t0
+    per_head_pairs = w.N * (w.N + 1) // 2 if causal else w.N * w.N
+    tflops = 14 * w.d * per_head_pairs * heads / dt / 1e12
+    return {"value": tflops, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {heads} of {w.B * w.H} heads of {name} in (b, h) order, fwd+bwd "
+                      f"in float64 with numpy, {dt:.1f} s wall",
+            "seconds": round(dt, 2)}
+
+
+def memory_sweep():
+    """Peak device memory of one fwd+bwd step (inputs, outputs, workspace) at
+    B=2, H=16, d=128, causal, for growing N: grows linearly in N."""
+    import torch
+    import io_aware_exact_11_amd as fa
+    out = []
+    for N in (2048, 4096, 8192, 16384, 32768):
+        torch.cuda.empty_cache()
+        torch.cuda.reset_peak_memory_stats()
+        base = torch.cuda.memory_allocated()
+        g = torch.Generator(device="cuda").manual_seed(N)
+        q, k, v, do = (torch.randn((2, 16, N, 128), device="cuda", generator=g, dtype=torch.bfloat16)
+                       for _ in range(4))
+        o, lse = fa.flash_attn_fwd(q, k, v, causal=True)
+        fa.flash_attn_bwd(q, k, v, o, do, lse, causal=True)
+        torch.cuda.synchronize()
+        peak = torch.cuda.max_memory_allocated() - base
+        out.append({"N": N, "peak_MiB": round(peak / 2**20, 1)})
+        del q, k, v, do, o, lse
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the N>=4096 workloads and the memory sweep")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="first run one device-to-device copy of this many MiB (HBM counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} requested, but this benchmark measures one GPU only; "
+              "attention shards over (batch, head) with no exchange, so run one process per GPU.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    import io_aware_exact_11_amd as fa
+    fa.load_library()
+
+    if args.copy_calibration_mib:
+        src = torch.ones(args.copy_calibration_mib * 2**18, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    case = Case(PRIMARY, causal=True)
+    wall_ms, fwd_ms, bwd_ms = case.run(args.steps, args.warmup)
+    ff, fb = case.flops()
+    value = (ff + fb) / (wall_ms * 1e-3) / 1e12
+    achieved = fb / (bwd_ms * 1e-3) / 1e12
+
+    traffic = None
+    try:
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("kernel_source_digest") == kernel_source_digest() and tr.get("workload") == PRIMARY:
+            traffic = tr.get("bwd_call_bytes")
+    except (OSError, ValueError):
+        pass
+
+    result = {
+        "metric": "attention fwd / fwd+bwd TFLOP/s (bf16) and % of MI355X MFMA peak, 1 GPU",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "gpt2_medium: B=64 H=16 N=1024 d=64 causal, fwd+bwd",
+                   "B": case.w.B, "H": case.w.H, "N": case.w.N, "d": case.w.d, "causal": True,
+                   "parallelism": "none (1 GPU)"},
+        "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "fwd_tflops": round(ff / (fwd_ms * 1e-3) / 1e12, 2),
+        "fwd_ms": round(fwd_ms, 4),
+        "bwd_ms": round(bwd_ms, 4),
+        "roofline": {"kernel": "flash_attn_bwd call (dQ fill + D pre-pass + main kernel)",
+                     "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic},
+    }
+    del case
+    torch.cuda.empty_cache()
+
+    if not args.no_extra:
+        extra = []
+        for name, causal in (("n4096_d128", False), ("n4096_d128", True), ("long_16k", True)):
+            c = Case(name, causal)
+            wms, fms, bms = c.run(args.steps, args.warmup)
+            cf, cb = c.flops()
+            extra.append({"workload": name, "causal": causal, "ms_per_step": round(wms, 4),
+                          "fwd_tflops": round(cf / (fms * 1e-3) / 1e12, 2),
+                          "fwd_frac": round(cf / (fms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                          "fwd_bwd_tflops": round((cf + cb) / (wms * 1e-3) / 1e12, 2),
+                          "fwd_bwd_frac": round((cf + cb) / (wms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)})
+            del c
+            torch.cuda.empty_cache()
+        result["workloads"] = extra
+        result["memory_sweep_B2_H16_d128_causal"] = memory_sweep()
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(PRIMARY, causal=True)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
