@@ -62,7 +62,12 @@ enum {
    * a bf16 high/low pair. Slower (about twice the matrix work), for inputs
    * whose gradients are large (e.g. outlier keys), where bf16 rounding of
    * O, P and dS dominates the error. */
-  FA_BWD_PRECISE = 1u << 0
+  FA_BWD_PRECISE = 1u << 0,
+  /* Accumulate dQ inside the key-outer kernel with fp32 atomics (one kernel
+   * doing the 5 algorithmic products) instead of the default pair of kernels
+   * that each write their outputs once (7 products' worth of work, no
+   * atomics). Kept for comparison; dQ is then not bitwise reproducible. */
+  FA_BWD_DQ_ATOMIC = 1u << 1
 };
 
 /*
@@ -82,9 +87,10 @@ int flash_attn_fwd(const void* Q, const void* K, const void* V, void* O, float* 
  * [B,H,N,d] outputs, fully overwritten. workspace: device memory of at least
  * flash_attn_bwd_workspace_bytes(B,H,N,d,flags) bytes, 256-byte aligned,
  * used for the per-row term D_i = sum_j P_ij dP_ij; its contents on entry
- * do not matter. flags: 0 or FA_BWD_PRECISE; any other bit is
- * FA_ERR_INVALID_ARG. dQ is accumulated with fp32 atomics, so it is not
- * bitwise reproducible from run to run; dK and dV are.
+ * do not matter. flags: any combination of FA_BWD_PRECISE and
+ * FA_BWD_DQ_ATOMIC; any other bit is FA_ERR_INVALID_ARG. By default every
+ * gradient is written exactly once and all three are bitwise reproducible;
+ * with FA_BWD_DQ_ATOMIC, dQ is accumulated with fp32 atomics and is not.
  */
 int flash_attn_bwd(const void* Q, const void* K, const void* V, const void* O,
                    const void* dO, const float* LSE, float* dQ, float* dK, float* dV,

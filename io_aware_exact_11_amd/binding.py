@@ -18,6 +18,7 @@ _lib = None
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
 FA_BWD_PRECISE = 1
+FA_BWD_DQ_ATOMIC = 2
 
 EXPORTED = ("flash_attn_fwd", "flash_attn_bwd", "flash_attn_bwd_workspace_bytes",
             "flash_attn_fwd_f32", "flash_attn_bwd_f32", "flash_attn_status_string")
@@ -157,9 +158,9 @@ def flash_attn_fwd_f32(q, k, v, causal=False, scale=None, kv_len=None, out=None,
 
 
 def flash_attn_bwd(q, k, v, o, do, lse, causal=False, scale=None, kv_len=None, precise=False,
-                   dq=None, dk=None, dv=None, workspace=None):
+                   dq_atomic=False, dq=None, dk=None, dv=None, workspace=None):
     """bf16 backward: returns fp32 (dQ, dK, dV)."""
-    flags = FA_BWD_PRECISE if precise else 0
+    flags = (FA_BWD_PRECISE if precise else 0) | (FA_BWD_DQ_ATOMIC if dq_atomic else 0)
     return _bwd("flash_attn_bwd", torch.bfloat16, q, k, v, o, do, lse, causal, scale, kv_len, flags,
                 dq, dk, dv, workspace)
 

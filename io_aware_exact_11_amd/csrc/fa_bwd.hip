@@ -485,47 +485,444 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
   }
 }
 
+// ---------------------------------------------------------------- split kernels
+//
+// Default backward: two kernels that each write their outputs once, no
+// atomics. dK, dV come from a key-outer kernel; dQ from a query-outer kernel
+// shaped like the forward. Both recompute S and dP, so together they do 7 of
+// the 5 algorithmic matrix products' worth of work, in exchange for no dQ
+// accumulation traffic and no cross-workgroup dependency.
+
+template <int D>
+struct DkdvCfg {
+  static constexpr int NW = 4;
+  static constexpr int BKV = 32 * NW;          // keys per workgroup (32 per wave)
+  static constexpr int BQ = 64;                // query rows per block
+  static constexpr int CH = BQ * D / 8 / 256;  // 16-byte chunks per thread per tensor
+};
+
+// dK, dV for 128 keys of one (b, h). The wave's K and V rows are B operands
+// held in registers; query blocks of Q and dO stream through swizzled,
+// double-buffered LDS tiles that serve as A operands both row-wise
+// (S = Q K^T, dP = dO V^T) and transposed (dV^T = dO^T P, dK^T = Q^T dS,
+// through ds_read_b64_tr_b16), with P and dS taken from registers.
+template <int D, bool PRECISE>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
+    const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
+    const u16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dg,
+    float* __restrict__ dK, float* __restrict__ dV, int H, int N, float scale, float sl2, int causal,
+    const int32_t* __restrict__ kv_len, int nkb, int total) {
+  using C = DkdvCfg<D>;
+  constexpr int BQ = C::BQ;
+  __shared__ __attribute__((aligned(16))) u16 Qs[2][BQ * D];
+  __shared__ __attribute__((aligned(16))) u16 dOs[2][BQ * D];
+  __shared__ __attribute__((aligned(16))) float lse2s[2][BQ];
+  __shared__ __attribute__((aligned(16))) float Ds[2][BQ];
+
+  const int tile = xcd_tile(blockIdx.x, total);
+  const int kbi = tile % nkb;  // ascending: causal key blocks with the most rows first
+  const int bh = tile / nkb;
+  const int b = bh / H;
+  const int kb0 = kbi * C::BKV;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, r = lane & 31, g = lane >> 5;
+  const int kw0 = kb0 + 32 * w;
+  const int key = kw0 + r;
+  const size_t head = (size_t)bh * N * D;
+  const unsigned head_bytes = (unsigned)N * D * 2;
+
+  int kv_lim = N;
+  if (kv_len) {
+    const int L = kv_len[b];
+    kv_lim = L < 0 ? 0 : (L > N ? N : L);
+  }
+
+  f32x16 dv[D / 32], dk[D / 32];
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      dv[t][e] = 0.f;
+      dk[t][e] = 0.f;
+    }
+
+  if (kb0 < kv_lim) {
+    const auto rQ = make_rsrc(Q + head, head_bytes);
+    const auto rK = make_rsrc(K + head, head_bytes);
+    const auto rV = make_rsrc(V + head, head_bytes);
+    const auto rO = make_rsrc(dO + head, head_bytes);
+    bf16x8 kf[D / 16], vf[D / 16];
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const unsigned off = (unsigned)(key * D + 16 * kk + 8 * g) * 2;
+      kf[kk] = as_bf16x8(ld_buf16(rK, off));
+      vf[kk] = as_bf16x8(ld_buf16(rV, off));
+    }
+
+    const int nqb = (N + BQ - 1) / BQ;
+    const int qb_start = causal ? kb0 / BQ : 0;
+    u32x4 qreg[C::CH], oreg[C::CH];
+    float lreg = 0.f, dreg = 0.f;
+    auto load = [&](int q0) {
+#pragma unroll
+      for (int rr = 0; rr < C::CH; ++rr) {
+        const int c = tid + 256 * rr;
+        const unsigned off = (unsigned)((q0 + c / (D / 8)) * D + (c % (D / 8)) * 8) * 2;
+        qreg[rr] = ld_buf16(rQ, off);
+        oreg[rr] = ld_buf16(rO, off);
+      }
+      if (tid < BQ) {
+        const int qq = q0 + tid;
+        lreg = qq < N ? LSE[(size_t)bh * N + qq] * kLog2e : INFINITY;
+        dreg = qq < N ? Dg[(size_t)bh * N + qq] : 0.f;
+      }
+    };
+    auto store = [&](int buf) {
+#pragma unroll
+      for (int rr = 0; rr < C::CH; ++rr) {
+        const int c = tid + 256 * rr;
+        const int off = swz_off<D>(c / (D / 8), (c % (D / 8)) * 8);
+        *reinterpret_cast<u32x4*>(&Qs[buf][off]) = qreg[rr];
+        *reinterpret_cast<u32x4*>(&dOs[buf][off]) = oreg[rr];
+      }
+      if (tid < BQ) {
+        lse2s[buf][tid] = lreg;
+        Ds[buf][tid] = dreg;
+      }
+    };
+    // Transposing-read coordinates of this lane (see ld_lds_tr): row part
+    // 4g + (lane % 16) / 4 inside a 16-row chunk, column part
+    // 16 * ((lane / 16) % 2) + 4 * (lane % 4) inside a 32-column tile.
+    const int tr_row = 4 * g + ((lane & 15) >> 2);
+    const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+    load(qb_start * BQ);
+    store(0);
+    __syncthreads();
+    for (int qb = qb_start; qb < nqb; ++qb) {
+      const int q0 = qb * BQ;
+      const int buf = (qb - qb_start) & 1;
+      if (qb + 1 < nqb) load(q0 + BQ);
+
+      if ((kw0 < kv_lim) && (!causal || q0 + BQ - 1 >= kw0)) {
+        // S = Q K^T, dP = dO V^T: rows = queries 32*qt + 8i + 4g + j, column = key.
+        f32x16 sa[BQ / 32], pa[BQ / 32];
+#pragma unroll
+        for (int qt = 0; qt < BQ / 32; ++qt) {
+          const int row = 32 * qt + r;
+          sa[qt] = mfma32_first(ld_lds16(&Qs[buf][swz_off<D>(row, 8 * g)]), kf[0]);
+          pa[qt] = mfma32_first(ld_lds16(&dOs[buf][swz_off<D>(row, 8 * g)]), vf[0]);
+#pragma unroll
+          for (int kk = 1; kk < D / 16; ++kk) {
+            sa[qt] = mfma32(ld_lds16(&Qs[buf][swz_off<D>(row, 16 * kk + 8 * g)]), kf[kk], sa[qt]);
+            pa[qt] = mfma32(ld_lds16(&dOs[buf][swz_off<D>(row, 16 * kk + 8 * g)]), vf[kk], pa[qt]);
+          }
+        }
+        const bool need_mask = (kw0 + 31 >= kv_lim) || (causal && q0 < kw0 + 31);
+#pragma unroll
+        for (int qt = 0; qt < BQ / 32; ++qt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int ql = 32 * qt + 8 * i + 4 * g;
+            const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse2s[buf][ql]);
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(&Ds[buf][ql]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int e = 4 * i + j;
+              float p = fast_exp2(sa[qt][e] * sl2 - l4[j]);
+              if (need_mask && (key >= kv_lim || (causal && key > q0 + ql + j))) p = 0.f;
+              sa[qt][e] = p;
+              pa[qt][e] = p * (pa[qt][e] - d4[j]);
+            }
+          }
+        bf16x8 pb[BQ / 16], db[BQ / 16], pl[PRECISE ? BQ / 16 : 1], dl[PRECISE ? BQ / 16 : 1];
+#pragma unroll
+        for (int c = 0; c < BQ / 16; ++c) {
+          if constexpr (PRECISE) {
+            pack_split_bf16x8(sa[c >> 1], 8 * (c & 1), pb[c], pl[c]);
+            pack_split_bf16x8(pa[c >> 1], 8 * (c & 1), db[c], dl[c]);
+          } else {
+            pb[c] = pack_bf16x8(sa[c >> 1], 8 * (c & 1));
+            db[c] = pack_bf16x8(pa[c >> 1], 8 * (c & 1));
+          }
+        }
+        // dV^T += dO^T P and dK^T += Q^T dS: A = the transposed tile (rows d =
+        // 32t + r, k-slots = queries 16c + 8h + 4g + 0..3 for slots 4h..4h+3),
+        // B = P / dS registers in the same slot order.
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+          for (int c = 0; c < BQ / 16; ++c) {
+            const int r0 = 16 * c + tr_row, col = 32 * t + tr_col;
+            const bf16x8 aO = join_tr(ld_lds_tr(&dOs[buf][swz_off<D>(r0, col)]),
+                                      ld_lds_tr(&dOs[buf][swz_off<D>(r0 + 8, col)]));
+            const bf16x8 aQ = join_tr(ld_lds_tr(&Qs[buf][swz_off<D>(r0, col)]),
+                                      ld_lds_tr(&Qs[buf][swz_off<D>(r0 + 8, col)]));
+            dv[t] = mfma32(aO, pb[c], dv[t]);
+            dk[t] = mfma32(aQ, db[c], dk[t]);
+            if constexpr (PRECISE) {
+              dv[t] = mfma32(aO, pl[c], dv[t]);
+              dk[t] = mfma32(aQ, dl[c], dk[t]);
+            }
+          }
+      }
+      if (qb + 1 < nqb) store(buf ^ 1);
+      __syncthreads();
+    }
+  }
+
+  if (key < N) {
+    float* dkrow = dK + head + (size_t)key * D;
+    float* dvrow = dV + head + (size_t)key * D;
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f32x4 a, c;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          a[j] = dk[t][4 * i + j] * scale;
+          c[j] = dv[t][4 * i + j];
+        }
+        *reinterpret_cast<f32x4*>(dkrow + 32 * t + 8 * i + 4 * g) = a;
+        *reinterpret_cast<f32x4*>(dvrow + 32 * t + 8 * i + 4 * g) = c;
+      }
+  }
+}
+
+template <int D>
+struct DqCfg {
+  static constexpr int NW = 4;
+  static constexpr int BR = 32 * NW;           // query rows per workgroup
+  static constexpr int BC = 64;                // keys per tile
+  static constexpr int VSTR = D + 8;           // padded V tile stride (row reads only)
+  static constexpr int CH = BC * D / 8 / 256;
+};
+
+// dQ for 128 query rows of one (b, h), written once. Shaped like the
+// forward: S^T = K Q^T and dP^T = V dO^T with the wave's Q and dO rows as B
+// operands, so each lane holds one query's P and dS for 32 keys of a tile;
+// dQ^T += K^T dS^T takes dS from those registers and K^T from the same
+// (swizzled) K tile through transposing reads.
+template <int D, bool PRECISE>
+__global__ __launch_bounds__(256, PRECISE ? 1 : 2) void bwd_dq_kernel(
+    const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
+    const u16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dg,
+    float* __restrict__ dQ, int H, int N, float scale, float sl2, int causal,
+    const int32_t* __restrict__ kv_len, int nqb, int total) {
+  using C = DqCfg<D>;
+  constexpr int BC = C::BC;
+  __shared__ __attribute__((aligned(16))) u16 Ks[2][BC * D];
+  __shared__ __attribute__((aligned(16))) u16 Vs[2][BC * C::VSTR];
+
+  const int tile = xcd_tile(blockIdx.x, total);
+  int qb = tile % nqb;
+  const int bh = tile / nqb;
+  if (causal) qb = nqb - 1 - qb;
+  const int b = bh / H;
+  const int q0 = qb * C::BR;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, r = lane & 31, g = lane >> 5;
+  const size_t head = (size_t)bh * N * D;
+  const unsigned head_bytes = (unsigned)N * D * 2;
+  const auto rQ = make_rsrc(Q + head, head_bytes);
+  const auto rK = make_rsrc(K + head, head_bytes);
+  const auto rV = make_rsrc(V + head, head_bytes);
+  const auto rO = make_rsrc(dO + head, head_bytes);
+
+  int kv_lim = N;
+  if (kv_len) {
+    const int L = kv_len[b];
+    kv_lim = L < 0 ? 0 : (L > N ? N : L);
+  }
+  int kv_end = kv_lim;
+  if (causal) kv_end = min(kv_end, q0 + C::BR);
+  const int nt = (kv_end + BC - 1) / BC;
+  const int q = q0 + 32 * w + r;
+  const int wave_q_first = q0 + 32 * w, wave_q_last = wave_q_first + 31;
+  const int nt_w = causal ? min(nt, wave_q_last / BC + 1) : nt;
+
+  bf16x8 qf[D / 16], df[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    const unsigned off = (unsigned)(q * D + 16 * kk + 8 * g) * 2;
+    qf[kk] = as_bf16x8(ld_buf16(rQ, off));
+    df[kk] = as_bf16x8(ld_buf16(rO, off));
+  }
+  const float lse2 = q < N ? LSE[(size_t)bh * N + q] * kLog2e : INFINITY;
+  const float Dq = q < N ? Dg[(size_t)bh * N + q] : 0.f;
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[t][e] = 0.f;
+
+  u32x4 kreg[C::CH], vreg[C::CH];
+  auto load = [&](int kb) {
+#pragma unroll
+    for (int rr = 0; rr < C::CH; ++rr) {
+      const int c = tid + 256 * rr;
+      const unsigned off = (unsigned)((kb + c / (D / 8)) * D + (c % (D / 8)) * 8) * 2;
+      kreg[rr] = ld_buf16(rK, off);
+      vreg[rr] = ld_buf16(rV, off);
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int rr = 0; rr < C::CH; ++rr) {
+      const int c = tid + 256 * rr;
+      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
+      *reinterpret_cast<u32x4*>(&Ks[buf][swz_off<D>(row, col)]) = kreg[rr];
+      *reinterpret_cast<u32x4*>(&Vs[buf][row * C::VSTR + col]) = vreg[rr];
+    }
+  };
+  const int tr_row = 4 * g + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+  if (nt > 0) {
+    load(0);
+    store(0);
+  }
+  __syncthreads();
+  for (int it = 0; it < nt; ++it) {
+    const int buf = it & 1;
+    const int kb = it * BC;
+    if (it + 1 < nt) load(kb + BC);
+    if (it < nt_w) {
+      f32x16 s[BC / 32], dp[BC / 32];
+#pragma unroll
+      for (int mt = 0; mt < BC / 32; ++mt) {
+        const int row = 32 * mt + r;
+        s[mt] = mfma32_first(ld_lds16(&Ks[buf][swz_off<D>(row, 8 * g)]), qf[0]);
+        dp[mt] = mfma32_first(ld_lds16(&Vs[buf][row * C::VSTR + 8 * g]), df[0]);
+#pragma unroll
+        for (int kk = 1; kk < D / 16; ++kk) {
+          s[mt] = mfma32(ld_lds16(&Ks[buf][swz_off<D>(row, 16 * kk + 8 * g)]), qf[kk], s[mt]);
+          dp[mt] = mfma32(ld_lds16(&Vs[buf][row * C::VSTR + 16 * kk + 8 * g]), df[kk], dp[mt]);
+        }
+      }
+      const bool need_mask = (kb + BC > kv_lim) || (causal && kb + BC - 1 > wave_q_first);
+#pragma unroll
+      for (int mt = 0; mt < BC / 32; ++mt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          float p = fast_exp2(s[mt][e] * sl2 - lse2);
+          if (need_mask) {
+            const int kk = kb + 32 * mt + 8 * (e >> 2) + 4 * g + (e & 3);
+            if (kk >= kv_lim || (causal && kk > q)) p = 0.f;
+          }
+          dp[mt][e] = p * (dp[mt][e] - Dq);
+        }
+      bf16x8 db[BC / 16], dl[PRECISE ? BC / 16 : 1];
+#pragma unroll
+      for (int c = 0; c < BC / 16; ++c) {
+        if constexpr (PRECISE)
+          pack_split_bf16x8(dp[c >> 1], 8 * (c & 1), db[c], dl[c]);
+        else
+          db[c] = pack_bf16x8(dp[c >> 1], 8 * (c & 1));
+      }
+      // dQ^T += K^T dS^T: A = K^T rows d = 32t + r, k-slots = keys of chunk c.
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+        for (int c = 0; c < BC / 16; ++c) {
+          const int r0 = 16 * c + tr_row, col = 32 * t + tr_col;
+          const bf16x8 aK = join_tr(ld_lds_tr(&Ks[buf][swz_off<D>(r0, col)]),
+                                    ld_lds_tr(&Ks[buf][swz_off<D>(r0 + 8, col)]));
+          acc[t] = mfma32(aK, db[c], acc[t]);
+          if constexpr (PRECISE) acc[t] = mfma32(aK, dl[c], acc[t]);
+        }
+    }
+    if (it + 1 < nt) store(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (q < N) {
+    float* row = dQ + head + (size_t)q * D;
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f32x4 a;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) a[j] = acc[t][4 * i + j] * scale;
+        *reinterpret_cast<f32x4*>(row + 32 * t + 8 * i + 4 * g) = a;
+      }
+  }
+}
+
 template <int D>
 static hipError_t launch_bwd_d(const void* Q, const void* K, const void* V, const void* O,
                                const void* dO, const float* LSE, float* dQ, float* dK, float* dV,
-                               float* Dws, const AttnShape& s, bool precise, hipStream_t stream) {
+                               float* Dws, const AttnShape& s, bool precise, bool dq_atomic,
+                               hipStream_t stream) {
   const size_t rows = (size_t)s.B * s.H * s.N;
   const float sl2 = s.scale * kLog2e;
-  hipError_t e = fill_zero(dQ, rows * D, stream);
-  if (e != hipSuccess) return e;
+  const u16* q = static_cast<const u16*>(Q);
+  const u16* k = static_cast<const u16*>(K);
+  const u16* v = static_cast<const u16*>(V);
+  const u16* o = static_cast<const u16*>(O);
+  const u16* g = static_cast<const u16*>(dO);
+  hipError_t e;
+  if (dq_atomic) {
+    e = fill_zero(dQ, rows * D, stream);
+    if (e != hipSuccess) return e;
+  }
   if (precise) {
     const int nqb = (s.N + ExactDCfg<D>::BR - 1) / ExactDCfg<D>::BR;
     const int total = s.B * s.H * nqb;
-    hipLaunchKernelGGL(bwd_exact_d_kernel<D>, dim3(total), dim3(256), 0, stream,
-                       static_cast<const u16*>(Q), static_cast<const u16*>(K),
-                       static_cast<const u16*>(V), static_cast<const u16*>(dO), LSE, Dws, s.H, s.N,
-                       sl2, s.causal, s.kv_len, nqb, total);
+    hipLaunchKernelGGL(bwd_exact_d_kernel<D>, dim3(total), dim3(256), 0, stream, q, k, v, g, LSE, Dws,
+                       s.H, s.N, sl2, s.causal, s.kv_len, nqb, total);
   } else {
     hipLaunchKernelGGL(bwd_dot_kernel<D>, dim3((unsigned)((rows * 16 + 255) / 256)), dim3(256), 0,
-                       stream, static_cast<const u16*>(O), static_cast<const u16*>(dO), Dws, (int)rows);
+                       stream, o, g, Dws, (int)rows);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int nkb = (s.N + BwdCfg<D>::BKV - 1) / BwdCfg<D>::BKV;
-  const int total = s.B * s.H * nkb;
-  if (precise)
-    hipLaunchKernelGGL((bwd_bf16_kernel<D, true>), dim3(total), dim3(256), 0, stream,
-                       static_cast<const u16*>(Q), static_cast<const u16*>(K),
-                       static_cast<const u16*>(V), static_cast<const u16*>(dO), LSE, Dws, dQ, dK, dV,
-                       s.H, s.N, s.scale, sl2, s.causal, s.kv_len, nkb, total);
-  else
-    hipLaunchKernelGGL((bwd_bf16_kernel<D, false>), dim3(total), dim3(256), 0, stream,
-                       static_cast<const u16*>(Q), static_cast<const u16*>(K),
-                       static_cast<const u16*>(V), static_cast<const u16*>(dO), LSE, Dws, dQ, dK, dV,
-                       s.H, s.N, s.scale, sl2, s.causal, s.kv_len, nkb, total);
+  if (dq_atomic) {
+    const int nkb = (s.N + BwdCfg<D>::BKV - 1) / BwdCfg<D>::BKV;
+    const int total = s.B * s.H * nkb;
+    if (precise)
+      hipLaunchKernelGGL((bwd_bf16_kernel<D, true>), dim3(total), dim3(256), 0, stream, q, k, v, g, LSE,
+                         Dws, dQ, dK, dV, s.H, s.N, s.scale, sl2, s.causal, s.kv_len, nkb, total);
+    else
+      hipLaunchKernelGGL((bwd_bf16_kernel<D, false>), dim3(total), dim3(256), 0, stream, q, k, v, g, LSE,
+                         Dws, dQ, dK, dV, s.H, s.N, s.scale, sl2, s.causal, s.kv_len, nkb, total);
+    return hipGetLastError();
+  }
+  {
+    const int nkb = (s.N + DkdvCfg<D>::BKV - 1) / DkdvCfg<D>::BKV;
+    const int total = s.B * s.H * nkb;
+    if (precise)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3(total), dim3(256), 0, stream, q, k, v, g, LSE,
+                         Dws, dK, dV, s.H, s.N, s.scale, sl2, s.causal, s.kv_len, nkb, total);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3(total), dim3(256), 0, stream, q, k, v, g, LSE,
+                         Dws, dK, dV, s.H, s.N, s.scale, sl2, s.causal, s.kv_len, nkb, total);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  {
+    const int nqb = (s.N + DqCfg<D>::BR - 1) / DqCfg<D>::BR;
+    const int total = s.B * s.H * nqb;
+    if (precise)
+      hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3(total), dim3(256), 0, stream, q, k, v, g, LSE,
+                         Dws, dQ, s.H, s.N, s.scale, sl2, s.causal, s.kv_len, nqb, total);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3(total), dim3(256), 0, stream, q, k, v, g, LSE,
+                         Dws, dQ, s.H, s.N, s.scale, sl2, s.causal, s.kv_len, nqb, total);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_bf16(const void* Q, const void* K, const void* V, const void* O,
                            const void* dO, const float* LSE, float* dQ, float* dK, float* dV,
-                           float* Dws, const AttnShape& s, bool precise, hipStream_t stream) {
-  if (s.d == 64) return launch_bwd_d<64>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, s, precise, stream);
-  return launch_bwd_d<128>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, s, precise, stream);
+                           float* Dws, const AttnShape& s, bool precise, bool dq_atomic,
+                           hipStream_t stream) {
+  if (s.d == 64)
+    return launch_bwd_d<64>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, s, precise, dq_atomic, stream);
+  return launch_bwd_d<128>(Q, K, V, O, dO, LSE, dQ, dK, dV, Dws, s, precise, dq_atomic, stream);
 }
 
 }  // namespace fa

@@ -28,6 +28,50 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
+
+// Raw buffer resource over `bytes` bytes at `base`: loads at offsets past
+// the end return 0, so tails need no branches. Word 3 = 0x00020000 selects
+// 32-bit raw (untyped) access.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 ld_buf16(__amdgpu_buffer_rsrc_t r, unsigned byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+}
+
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16). Within each group of 16
+// lanes, lane i receives in slot t the (i % 4)-th 16-bit element of the 8
+// bytes addressed by lane 4t + i/4 of its group. When lane j of a group
+// addresses row (r0 + j/4), columns (c0 + 4(j%4)) .. +3 of a row-major
+// bf16 tile, lane i receives column c0 + i of rows r0 .. r0+3.
+__device__ __forceinline__ s16x4 ld_lds_tr(const u16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+}
+
+__device__ __forceinline__ bf16x8 join_tr(s16x4 lo, s16x4 hi) {
+  typedef __attribute__((__vector_size__(8 * sizeof(short)))) short s16x8;
+  const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Maximum of x over the lane pair (l, l ^ 32), returned on both lanes.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+__device__ __forceinline__ f32x16 mfma32_first(bf16x8 a, bf16x8 b) {
+  const f32x16 z = {};
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, z, 0, 0, 0);
+}
+
 __device__ __forceinline__ u32x4 ld_global16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
@@ -69,6 +113,23 @@ __device__ __forceinline__ unsigned bf16_bits(const u32x4& v, int e) {
 // 8i+4g+j of an earlier product, i in {2h, 2h+1}) are 8 adjacent columns.
 __device__ __forceinline__ int swap23(int x) {
   return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1);
+}
+
+// 16-byte chunk swizzle for unpadded row-major bf16 tiles of width D that
+// are read both by rows (one 16-byte chunk per lane, 16 consecutive rows per
+// LDS cycle) and transposed (ds_read_b64_tr_b16: 4 consecutive rows x 4
+// chunks per 32 lanes). Chunk c of row r is stored at chunk c ^ swz(r); with
+// 64 four-byte banks both access patterns then touch distinct banks.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+// Element offset of (row r, column col) in a swizzled tile; col % 8 is kept.
+template <int D>
+__device__ __forceinline__ int swz_off(int r, int col) {
+  return r * D + ((((col >> 3) ^ swz<D>(r)) << 3) | (col & 7));
 }
 
 // Map a linear workgroup id to a tile id so that the tiles of one (b, h)

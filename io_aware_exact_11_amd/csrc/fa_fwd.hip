@@ -23,8 +23,14 @@
 //
 // The P~ V product reuses the score registers directly as its B operand
 // (O^T = V^T P^T): the 8 k-slots a lane feeds are 8 of its own score
-// elements. Its A operand needs V transposed, so V tiles are written to LDS
-// as V^T with their key columns permuted by swap23 to match those slots.
+// elements. Its A operand is V transposed; V tiles stay row-major in LDS and
+// are read transposed with ds_read_b64_tr_b16, two reads per operand, with
+// the key order chosen to match those slots.
+//
+// The running maximum moves lazily: only when a tile's maximum exceeds it by
+// more than 8 (base 2), which keeps every weight below 2^8 and skips the O
+// rescale on almost every tile. Loads go through buffer resources, whose
+// hardware bounds check returns zeros past the end of a head.
 #include "fa_common.h"
 #include "fa_launch.h"
 
@@ -36,13 +42,15 @@ struct FwdCfg {
   static constexpr int BR = 32 * NW;            // query rows per workgroup
   static constexpr int BC = 64;                 // keys per tile
   static constexpr int KSTR = D + 8;            // K tile row stride (elements)
-  static constexpr int VSTR = BC + 8;           // V^T tile row stride (elements)
-  static constexpr int KCH = BC * D / 8 / 256;  // 16-byte K chunks per thread
-  static constexpr int VKR = BC * D / 8 / 256;  // keys per thread in the V^T store
-  static constexpr int NKG = BC / VKR;          // key groups in the V^T store
+  static constexpr int VSTR = D + 32;           // V tile row stride: the 4 rows of a transposing read land 16 banks apart
+  static constexpr int CH = BC * D / 8 / 256;   // 16-byte chunks per thread per tile
   static_assert(D == 64 || D == 128, "head dim");
-  static_assert(NKG * (D / 8) == 256, "V^T store covers the tile once");
 };
+
+// Rescale threshold, in base-2 units of the scaled score: the running
+// maximum only moves (and O, l are only rescaled) when a tile's maximum
+// exceeds it by more than this, so unnormalised weights stay below 2^8.
+constexpr float kRescaleSlack = 8.f;
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
@@ -52,7 +60,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   using C = FwdCfg<D>;
   constexpr int BC = C::BC;
   __shared__ __attribute__((aligned(16))) u16 Ks[2][BC * C::KSTR];
-  __shared__ __attribute__((aligned(16))) u16 Vt[2][D * C::VSTR];
+  __shared__ __attribute__((aligned(16))) u16 Vs[2][BC * C::VSTR];
 
   const int tile = xcd_tile(blockIdx.x, total);
   int qb = tile % nqb;
@@ -63,8 +71,10 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, r = lane & 31, g = lane >> 5;
   const size_t head = (size_t)bh * N * D;
-  const u16* Kh = K + head;
-  const u16* Vh = V + head;
+  const unsigned head_bytes = (unsigned)N * D * 2;
+  const auto rQ = make_rsrc(Q + head, head_bytes);
+  const auto rK = make_rsrc(K + head, head_bytes);
+  const auto rV = make_rsrc(V + head, head_bytes);
 
   int kv_lim = N;
   if (kv_len) {
@@ -79,13 +89,11 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   const int wave_q_first = q0 + 32 * w;
   const int wave_q_last = wave_q_first + 31;
 
+  // Q fragment: B operand of S^T = K Q^T (column = query, k = d).
   bf16x8 qf[D / 16];
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) {
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (q < N) v = ld_global16(Q + head + (size_t)q * D + 16 * kk + 8 * g);
-    qf[kk] = as_bf16x8(v);
-  }
+  for (int kk = 0; kk < D / 16; ++kk)
+    qf[kk] = as_bf16x8(ld_buf16(rQ, (unsigned)(q * D + 16 * kk + 8 * g) * 2));
 
   f32x16 o[D / 32];
 #pragma unroll
@@ -94,70 +102,74 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     for (int e = 0; e < 16; ++e) o[t][e] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
-  u32x4 kreg[C::KCH], vreg[C::VKR];
-  const int vkg = tid % C::NKG, vdc = tid / C::NKG;
-
-  auto load_tile = [&](int kb) {
-#pragma unroll
-    for (int rr = 0; rr < C::KCH; ++rr) {
-      const int c = tid + 256 * rr;
-      const int key = kb + c / (D / 8);
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (key < N) v = ld_global16(Kh + (size_t)key * D + (c % (D / 8)) * 8);
-      kreg[rr] = v;
-    }
-#pragma unroll
-    for (int rr = 0; rr < C::VKR; ++rr) {
-      const int key = kb + vkg * C::VKR + rr;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (key < N) v = ld_global16(Vh + (size_t)key * D + vdc * 8);
-      vreg[rr] = v;
-    }
+  // Tile loads: chunk c = tid + 256*rr is row c / (D/8), 16-byte column c % (D/8).
+  u32x4 kreg[C::CH], vreg[C::CH];
+  auto tile_off = [&](int kb, int rr) {
+    const int c = tid + 256 * rr;
+    return (unsigned)((kb + c / (D / 8)) * D + (c % (D / 8)) * 8) * 2;
   };
-  auto store_tile = [&](int buf) {
+  auto load_k = [&](int kb) {
 #pragma unroll
-    for (int rr = 0; rr < C::KCH; ++rr) {
+    for (int rr = 0; rr < C::CH; ++rr) kreg[rr] = ld_buf16(rK, tile_off(kb, rr));
+  };
+  auto load_v = [&](int kb) {
+#pragma unroll
+    for (int rr = 0; rr < C::CH; ++rr) vreg[rr] = ld_buf16(rV, tile_off(kb, rr));
+  };
+  auto store_k = [&](int buf) {
+#pragma unroll
+    for (int rr = 0; rr < C::CH; ++rr) {
       const int c = tid + 256 * rr;
       *reinterpret_cast<u32x4*>(&Ks[buf][(c / (D / 8)) * C::KSTR + (c % (D / 8)) * 8]) = kreg[rr];
     }
-    const int col = swap23(vkg * C::VKR);
+  };
+  auto store_v = [&](int buf) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      u16* dst = &Vt[buf][(vdc * 8 + e) * C::VSTR + col];
-      if constexpr (C::VKR == 4) {
-        u32x2 p;
-        p[0] = bf16_bits(vreg[0], e) | (bf16_bits(vreg[1], e) << 16);
-        p[1] = bf16_bits(vreg[2], e) | (bf16_bits(vreg[3], e) << 16);
-        *reinterpret_cast<u32x2*>(dst) = p;
-      } else {
-        *reinterpret_cast<unsigned*>(dst) = bf16_bits(vreg[0], e) | (bf16_bits(vreg[1], e) << 16);
-      }
+    for (int rr = 0; rr < C::CH; ++rr) {
+      const int c = tid + 256 * rr;
+      *reinterpret_cast<u32x4*>(&Vs[buf][(c / (D / 8)) * C::VSTR + (c % (D / 8)) * 8]) = vreg[rr];
     }
   };
+  // S^T tile from K buffer `buf`: rows = keys 32*mt + (8i + 4g + j), column = query q.
+  auto qk = [&](int buf, f32x16* s) {
+#pragma unroll
+    for (int mt = 0; mt < BC / 32; ++mt) {
+      const u16* kp = &Ks[buf][(32 * mt + r) * C::KSTR + 8 * g];
+      s[mt] = mfma32_first(ld_lds16(kp), qf[0]);
+#pragma unroll
+      for (int kk = 1; kk < D / 16; ++kk) s[mt] = mfma32(ld_lds16(kp + 16 * kk), qf[kk], s[mt]);
+    }
+  };
+  // Per-lane offsets of the transposing V reads (see ld_lds_tr): row part
+  // 4g + (lane % 16) / 4, column part 16 * ((lane / 16) % 2) + 4 * (lane % 4).
+  const int v_tr_off = (4 * g + ((lane & 15) >> 2)) * C::VSTR + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  // Causal waves compute only the tiles that reach their rows (a prefix).
+  const int nt_w = causal ? min(nt, wave_q_last / BC + 1) : nt;
 
+  // Software pipeline: K runs one tile ahead of V, so while tile j's softmax
+  // is on the vector ALUs the wave already issues tile j+1's S^T products.
+  // Buffers: K_j in Ks[j % 2], V_j in Vs[j % 2]; one barrier per tile.
   if (nt > 0) {
-    load_tile(0);
-    store_tile(0);
+    load_k(0);
+    load_v(0);
+    store_k(0);
+    store_v(0);
+  }
+  if (nt > 1) {
+    load_k(BC);
+    store_k(1);
   }
   __syncthreads();
+  f32x16 s_cur[BC / 32];
+  if (nt_w > 0) qk(0, s_cur);
 
   for (int it = 0; it < nt; ++it) {
-    const int buf = it & 1;
     const int kb = it * BC;
-    if (it + 1 < nt) load_tile(kb + BC);
+    const bool more_k = it + 2 < nt, more_v = it + 1 < nt;
+    if (more_k) load_k(kb + 2 * BC);
+    if (more_v) load_v(kb + BC);
 
-    if (!causal || kb <= wave_q_last) {
-      // S^T tile: rows = keys kb + 32*mt + (8i + 4g + j), column = query q.
-      f32x16 s[BC / 32];
-#pragma unroll
-      for (int mt = 0; mt < BC / 32; ++mt) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) s[mt][e] = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk)
-          s[mt] = mfma32(ld_lds16(&Ks[buf][(32 * mt + r) * C::KSTR + 16 * kk + 8 * g]), qf[kk], s[mt]);
-      }
-
+    if (it < nt_w) {
       const bool need_mask = (kb + BC > kv_lim) || (causal && kb + BC - 1 > wave_q_first);
       if (need_mask) {
 #pragma unroll
@@ -165,50 +177,68 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
             const int key = kb + 32 * mt + 8 * (e >> 2) + 4 * g + (e & 3);
-            if (key >= kv_lim || (causal && key > q)) s[mt][e] = -INFINITY;
+            if (key >= kv_lim || (causal && key > q)) s_cur[mt][e] = -INFINITY;
           }
       }
 
-      float mx = -INFINITY;
+      float mx = s_cur[0][0];
 #pragma unroll
       for (int mt = 0; mt < BC / 32; ++mt)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[mt][e]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx * sl2);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
+        for (int e = (mt == 0 ? 1 : 0); e < 16; ++e) mx = fmaxf(mx, s_cur[mt][e]);
+      const float tmax = pair_max(mx) * sl2;
+      // Move the reference maximum only when some row of the wave outgrows it.
+      if (__builtin_amdgcn_ballot_w64(tmax > m_run + kRescaleSlack) != 0) {
+        const float m_new = fmaxf(m_run, tmax);
+        const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) o[t][e] *= alpha;
+        m_run = m_new;
+      }
+      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+
+      // Next tile's scores (on the last tile this reads a stale buffer and
+      // the result is dropped), independent of the softmax below.
+      f32x16 s_next[BC / 32];
+      qk((it + 1) & 1, s_next);
+
       float rs = 0.f;
 #pragma unroll
       for (int mt = 0; mt < BC / 32; ++mt)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const float p = fast_exp2(s[mt][e] * sl2 - m_use);
-          s[mt][e] = p;
+          const float p = fast_exp2(s_cur[mt][e] * sl2 - m_use);
+          s_cur[mt][e] = p;
           rs += p;
         }
-      l_run = l_run * alpha + rs;
-      m_run = m_new;
-#pragma unroll
-      for (int t = 0; t < D / 32; ++t)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) o[t][e] *= alpha;
+      l_run += rs;
 
       bf16x8 pb[BC / 16];
 #pragma unroll
-      for (int c = 0; c < BC / 16; ++c) pb[c] = pack_bf16x8(s[c >> 1], 8 * (c & 1));
+      for (int c = 0; c < BC / 16; ++c) pb[c] = pack_bf16x8(s_cur[c >> 1], 8 * (c & 1));
+      // O^T += V^T P^T: A = V^T rows d = 32t + r, k-slots = keys of chunk c in
+      // the order of the score registers (16c + 8h + 4g + 0..3 for slots 4h..4h+3).
+      const u16* vb = &Vs[it & 1][v_tr_off];
 #pragma unroll
       for (int t = 0; t < D / 32; ++t)
 #pragma unroll
-        for (int c = 0; c < BC / 16; ++c)
-          o[t] = mfma32(ld_lds16(&Vt[buf][(32 * t + r) * C::VSTR + 16 * c + 8 * g]), pb[c], o[t]);
+        for (int c = 0; c < BC / 16; ++c) {
+          const u16* vp = vb + (16 * c) * C::VSTR + 32 * t;
+          o[t] = mfma32(join_tr(ld_lds_tr(vp), ld_lds_tr(vp + 8 * C::VSTR)), pb[c], o[t]);
+        }
+#pragma unroll
+      for (int mt = 0; mt < BC / 32; ++mt) s_cur[mt] = s_next[mt];
     }
 
-    if (it + 1 < nt) store_tile(buf ^ 1);
+    if (more_k) store_k(it & 1);
+    if (more_v) store_v((it + 1) & 1);
     __syncthreads();
   }
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = pair_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (q < N) {
     u16* orow = O + head + (size_t)q * D;

@@ -22,7 +22,8 @@ hipError_t launch_fwd_bf16(const void* Q, const void* K, const void* V, void* O,
 // Dws: fp32 [B,H,N] scratch for the per-row term D_i.
 hipError_t launch_bwd_bf16(const void* Q, const void* K, const void* V, const void* O,
                            const void* dO, const float* LSE, float* dQ, float* dK, float* dV,
-                           float* Dws, const AttnShape& s, bool precise, hipStream_t stream);
+                           float* Dws, const AttnShape& s, bool precise, bool dq_atomic,
+                           hipStream_t stream);
 
 hipError_t launch_fwd_f32(const float* Q, const float* K, const float* V, float* O, float* LSE,
                           const AttnShape& s, hipStream_t stream);

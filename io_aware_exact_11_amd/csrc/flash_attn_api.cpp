@@ -109,11 +109,12 @@ int flash_attn_bwd(const void* Q, const void* K, const void* V, const void* O, c
                    size_t workspace_bytes_, int B, int H, int N, int d, float scale, int causal,
                    const int32_t* kv_len, unsigned flags, void* stream) {
   const int st = bwd_common(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, workspace_bytes_, B, H, N, d,
-                            scale, causal, flags, FA_BWD_PRECISE, 2);
+                            scale, causal, flags, FA_BWD_PRECISE | FA_BWD_DQ_ATOMIC, 2);
   if (st != FA_OK) return st;
   const fa::AttnShape s{B, H, N, d, scale, causal, kv_len};
   return hip_status(fa::launch_bwd_bf16(Q, K, V, O, dO, LSE, dQ, dK, dV, static_cast<float*>(workspace),
                                         s, (flags & FA_BWD_PRECISE) != 0,
+                                        (flags & FA_BWD_DQ_ATOMIC) != 0,
                                         static_cast<hipStream_t>(stream)));
 }
 

@@ -29,13 +29,13 @@ def _fa():
     return fa
 
 
-def _run_bf16(x, causal, scale, kv, precise=False):
+def _run_bf16(x, causal, scale, kv, precise=False, dq_atomic=False):
     fa = _fa()
     q, k, v, do = (dev_bf16(x[n + "_bits"]) for n in ("Q", "K", "V", "dO"))
     kvd = dev_kv(kv)
     o, lse = fa.flash_attn_fwd(q, k, v, causal=causal, scale=scale, kv_len=kvd)
     dq, dk, dv = fa.flash_attn_bwd(q, k, v, o, do, lse, causal=causal, scale=scale, kv_len=kvd,
-                                   precise=precise)
+                                   precise=precise, dq_atomic=dq_atomic)
     torch.cuda.synchronize()
     return o, lse, dq, dk, dv
 
@@ -73,12 +73,14 @@ SMALL = [
 ]
 
 
+@pytest.mark.parametrize("dq_atomic", [False, True], ids=["split", "atomic"])
 @pytest.mark.parametrize("B,H,N,d,causal,padded,precise", SMALL)
-def test_small_full_compare(B, H, N, d, causal, padded, precise):
-    log(f"small B={B} H={H} N={N} d={d} causal={causal} padded={padded} precise={precise}")
+def test_small_full_compare(B, H, N, d, causal, padded, precise, dq_atomic):
+    log(f"small B={B} H={H} N={N} d={d} causal={causal} padded={padded} precise={precise} "
+        f"dq_atomic={dq_atomic}")
     x = wl.make_inputs(B, H, N, d, seed=100 + N + d, padded=padded)
     scale = float(np.float32(d ** -0.5))
-    got = _run_bf16(x, causal, scale, x["kv_len"], precise=precise)
+    got = _run_bf16(x, causal, scale, x["kv_len"], precise=precise, dq_atomic=dq_atomic)
     heads = [(b, h) for b in range(B) for h in range(H)]
     _check_heads(x, got, causal, scale, x["kv_len"], heads)
 
@@ -160,8 +162,9 @@ def test_fp32_entry_points_masks():
 
 
 def test_forward_is_bitwise_reproducible_and_overwrites_outputs():
-    """Two runs agree bit for bit (O, LSE, dK, dV); NaN-poisoned outputs are
-    fully overwritten and guard bands around them stay untouched."""
+    """Two runs agree bit for bit (O, LSE and, by default, dQ, dK, dV);
+    NaN-poisoned outputs are fully overwritten and guard bands around them
+    stay untouched; the atomic-dQ variant agrees with the default."""
     fa = _fa()
     B, H, N, d = 2, 4, 500, 128
     x = wl.make_inputs(B, H, N, d, seed=5)
@@ -192,8 +195,11 @@ def test_forward_is_bitwise_reproducible_and_overwrites_outputs():
     torch.cuda.synchronize()
     for t in g1:
         assert not torch.any(torch.isnan(t))
-    assert torch.equal(g1[1], g2[1]) and torch.equal(g1[2], g2[2])
-    assert torch.allclose(g1[0], g2[0], atol=1e-5, rtol=0)
+    assert torch.equal(g1[0], g2[0]) and torch.equal(g1[1], g2[1]) and torch.equal(g1[2], g2[2])
+    g3 = fa.flash_attn_bwd(q, k, v, o, do, lse, causal=True, dq_atomic=True)
+    torch.cuda.synchronize()
+    for a, c in zip(g3, g2):
+        assert torch.allclose(a, c, atol=1e-4, rtol=0)
 
 
 FULL = [
