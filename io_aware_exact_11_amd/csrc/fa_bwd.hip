@@ -497,8 +497,11 @@ template <int D>
 struct DkdvCfg {
   static constexpr int NW = 4;
   static constexpr int BKV = 32 * NW;          // keys per workgroup (32 per wave)
-  static constexpr int BQ = 64;                // query rows per block
+  // query rows per block: 64 at d=128; 32 at d=64, where the smaller blocks
+  // measured faster (shorter sequences, lighter per-block products)
+  static constexpr int BQ = D == 128 ? 64 : 32;
   static constexpr int CH = BQ * D / 8 / 256;  // 16-byte chunks per thread per tensor
+  static_assert(CH >= 1, "one chunk per thread at least");
 };
 
 // dK, dV for 128 keys of one (b, h). The wave's K and V rows are B operands
@@ -618,7 +621,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
             pa[qt] = mfma32(ld_lds16(&dOs[buf][swz_off<D>(row, 16 * kk + 8 * g)]), vf[kk], pa[qt]);
           }
         }
-        const bool need_mask = (kw0 + 31 >= kv_lim) || (causal && q0 < kw0 + 31);
+        // Masked scores become -inf, so their weights come out exactly 0.
+        if ((kw0 + 31 >= kv_lim) || (causal && q0 < kw0 + 31)) {
+#pragma unroll
+          for (int qt = 0; qt < BQ / 32; ++qt)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const int qq = q0 + 32 * qt + 8 * (e >> 2) + 4 * g + (e & 3);
+              const bool off = (key >= kv_lim) | ((causal != 0) & (key > qq));
+              sa[qt][e] = off ? -INFINITY : sa[qt][e];
+            }
+        }
 #pragma unroll
         for (int qt = 0; qt < BQ / 32; ++qt)
 #pragma unroll
@@ -629,8 +642,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               const int e = 4 * i + j;
-              float p = fast_exp2(sa[qt][e] * sl2 - l4[j]);
-              if (need_mask && (key >= kv_lim || (causal && key > q0 + ql + j))) p = 0.f;
+              const float p = fast_exp2(sa[qt][e] * sl2 - l4[j]);
               sa[qt][e] = p;
               pa[qt][e] = p * (pa[qt][e] - d4[j]);
             }
@@ -802,16 +814,21 @@ __global__ __launch_bounds__(256, PRECISE ? 1 : 2) void bwd_dq_kernel(
           dp[mt] = mfma32(ld_lds16(&Vs[buf][row * C::VSTR + 16 * kk + 8 * g]), df[kk], dp[mt]);
         }
       }
-      const bool need_mask = (kb + BC > kv_lim) || (causal && kb + BC - 1 > wave_q_first);
+      if ((kb + BC > kv_lim) || (causal && kb + BC - 1 > wave_q_first)) {
+#pragma unroll
+        for (int mt = 0; mt < BC / 32; ++mt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int kk = kb + 32 * mt + 8 * (e >> 2) + 4 * g + (e & 3);
+            const bool off = (kk >= kv_lim) | ((causal != 0) & (kk > q));
+            s[mt][e] = off ? -INFINITY : s[mt][e];
+          }
+      }
 #pragma unroll
       for (int mt = 0; mt < BC / 32; ++mt)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          float p = fast_exp2(s[mt][e] * sl2 - lse2);
-          if (need_mask) {
-            const int kk = kb + 32 * mt + 8 * (e >> 2) + 4 * g + (e & 3);
-            if (kk >= kv_lim || (causal && kk > q)) p = 0.f;
-          }
+          const float p = fast_exp2(s[mt][e] * sl2 - lse2);
           dp[mt][e] = p * (dp[mt][e] - Dq);
         }
       bf16x8 db[BC / 16], dl[PRECISE ? BC / 16 : 1];

@@ -177,7 +177,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
             const int key = kb + 32 * mt + 8 * (e >> 2) + 4 * g + (e & 3);
-            if (key >= kv_lim || (causal && key > q)) s_cur[mt][e] = -INFINITY;
+            const bool off = (key >= kv_lim) | ((causal != 0) & (key > q));
+            s_cur[mt][e] = off ? -INFINITY : s_cur[mt][e];
           }
       }
 

@@ -1,7 +1,7 @@
 // extern "C" entry points of libflashattn.so: argument checks on the host,
 // then dispatch to the gfx950 launchers. Nothing is enqueued unless every
 // check passes.
-#include "../../include/flash_attn.h"
+#include "flash_attn.h"
 
 #include <math.h>
 #include <stdint.h>
