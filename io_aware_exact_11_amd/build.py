@@ -18,9 +18,13 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libflashattn.so")
 SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_f32.hip", "flash_attn_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-# Packed fp32 VALU forms are switched off for all device code.
+# Packed fp32 VALU forms are switched off for all device code. Matrix-core
+# products keep their accumulators in VGPRs (-amdgpu-mfma-vgpr-form): the
+# default heuristic parks them in AGPRs and copies them back and forth around
+# every product in the register-heavy backward kernels.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
-         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 
 
 def _run(cmd):
