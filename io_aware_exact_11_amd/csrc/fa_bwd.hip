@@ -207,291 +207,15 @@ __global__ __launch_bounds__(256, 2) void bwd_exact_d_kernel(
   if (q < N && g == 0) Dout[(size_t)bh * N + q] = part;
 }
 
-// ---------------------------------------------------------------- main kernel
-
-template <int D>
-struct BwdCfg {
-  static constexpr int NW = 4;
-  static constexpr int BKV = 32 * NW;               // keys per workgroup
-  static constexpr int BQ = 64;                     // query rows per block
-  static constexpr int QSTR = D + 8;                // row-major Q / dO tile stride
-  static constexpr int TSTR = BQ + 8;               // transposed Q / dO tile stride
-  static constexpr int KTSTR = BKV + 8;             // K^T tile stride
-  static constexpr int DSSTR = BKV + 8;             // dS tile stride
-  static constexpr int UQ = BQ * D / 8 / 256;       // query rows per thread in a tile load
-  static constexpr int NQG = BQ / UQ;
-  static constexpr int UK = BKV * D / 8 / 256;      // key rows per thread in the K^T store
-  static constexpr int NKG = BKV / UK;
-  static_assert(NQG * (D / 8) == 256 && NKG * (D / 8) == 256, "one pass per tile");
-  static constexpr size_t LDS_BYTES =
-      2 * (2 * BQ * QSTR + 2 * D * TSTR) + 2 * D * KTSTR + 2 * BQ * DSSTR + 8 * BQ;
-};
-
-template <int D, bool PRECISE>
-__global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
-    const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
-    const u16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dg,
-    float* __restrict__ dQ, float* __restrict__ dK, float* __restrict__ dV, int H, int N,
-    float scale, float sl2, int causal, const int32_t* __restrict__ kv_len, int nkb, int total) {
-  using C = BwdCfg<D>;
-  constexpr int BQ = C::BQ;
-  __shared__ __attribute__((aligned(16))) u16 Qs[BQ * C::QSTR];
-  __shared__ __attribute__((aligned(16))) u16 dOs[BQ * C::QSTR];
-  __shared__ __attribute__((aligned(16))) u16 QT[D * C::TSTR];
-  __shared__ __attribute__((aligned(16))) u16 dOT[D * C::TSTR];
-  __shared__ __attribute__((aligned(16))) u16 KT[D * C::KTSTR];
-  // dS tile; in precise mode followed by the low half of its bf16 split.
-  __shared__ __attribute__((aligned(16))) u16 dSs[(PRECISE ? 2 : 1) * BQ * C::DSSTR];
-  __shared__ __attribute__((aligned(16))) float lse2s[BQ];
-  __shared__ __attribute__((aligned(16))) float Ds[BQ];
-
-  const int tile = xcd_tile(blockIdx.x, total);
-  const int kbi = tile % nkb;  // ascending: causal key blocks with the most rows first
-  const int bh = tile / nkb;
-  const int b = bh / H;
-  const int kb0 = kbi * C::BKV;
-  const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, r = lane & 31, g = lane >> 5;
-  const int kw0 = kb0 + 32 * w;
-  const int key = kw0 + r;  // this lane's key (column of S, dP, dV^T, dK^T)
-  const size_t head = (size_t)bh * N * D;
-
-  int kv_lim = N;
-  if (kv_len) {
-    const int L = kv_len[b];
-    kv_lim = L < 0 ? 0 : (L > N ? N : L);
-  }
-
-  f32x16 dv[D / 32], dk[D / 32];
-#pragma unroll
-  for (int t = 0; t < D / 32; ++t)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      dv[t][e] = 0.f;
-      dk[t][e] = 0.f;
-    }
-
-  if (kb0 < kv_lim) {
-    // K and V rows of this lane's key as B operands (column = key, k = d).
-    bf16x8 kf[D / 16], vf[D / 16];
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      u32x4 a = {0u, 0u, 0u, 0u}, c = {0u, 0u, 0u, 0u};
-      if (key < N) {
-        a = ld_global16(K + head + (size_t)key * D + 16 * kk + 8 * g);
-        c = ld_global16(V + head + (size_t)key * D + 16 * kk + 8 * g);
-      }
-      kf[kk] = as_bf16x8(a);
-      vf[kk] = as_bf16x8(c);
-    }
-    // K^T tile of the workgroup's keys, for the dQ product's B operand.
-    {
-      const int kg = tid % C::NKG, dc = tid / C::NKG;
-      u32x4 kr[C::UK];
-#pragma unroll
-      for (int rr = 0; rr < C::UK; ++rr) {
-        const int kk = kb0 + kg * C::UK + rr;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (kk < N) v = ld_global16(K + head + (size_t)kk * D + dc * 8);
-        kr[rr] = v;
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        u16* dst = &KT[(dc * 8 + e) * C::KTSTR + kg * C::UK];
-#pragma unroll
-        for (int rr = 0; rr < C::UK; rr += 2)
-          *reinterpret_cast<unsigned*>(dst + rr) = bf16_bits(kr[rr], e) | (bf16_bits(kr[rr + 1], e) << 16);
-      }
-    }
-
-    const int nqb = (N + BQ - 1) / BQ;
-    const int qb_start = causal ? kb0 / BQ : 0;
-    const int qg = tid % C::NQG, qdc = tid / C::NQG;
-    u32x4 qreg[C::UQ], oreg[C::UQ];
-    float lse_reg = 0.f, d_reg = 0.f;
-
-    auto load_q = [&](int q0) {
-#pragma unroll
-      for (int rr = 0; rr < C::UQ; ++rr) {
-        const int qq = q0 + qg * C::UQ + rr;
-        u32x4 a = {0u, 0u, 0u, 0u}, c = {0u, 0u, 0u, 0u};
-        if (qq < N) {
-          a = ld_global16(Q + head + (size_t)qq * D + qdc * 8);
-          c = ld_global16(dO + head + (size_t)qq * D + qdc * 8);
-        }
-        qreg[rr] = a;
-        oreg[rr] = c;
-      }
-      if (tid < BQ) {
-        const int qq = q0 + tid;
-        lse_reg = qq < N ? LSE[(size_t)bh * N + qq] * kLog2e : INFINITY;
-        d_reg = qq < N ? Dg[(size_t)bh * N + qq] : 0.f;
-      }
-    };
-    auto store_q = [&]() {
-#pragma unroll
-      for (int rr = 0; rr < C::UQ; ++rr) {
-        const int row = qg * C::UQ + rr;
-        *reinterpret_cast<u32x4*>(&Qs[row * C::QSTR + qdc * 8]) = qreg[rr];
-        *reinterpret_cast<u32x4*>(&dOs[row * C::QSTR + qdc * 8]) = oreg[rr];
-      }
-      const int col = swap23(qg * C::UQ);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        u16* dq_ = &QT[(qdc * 8 + e) * C::TSTR + col];
-        u16* do_ = &dOT[(qdc * 8 + e) * C::TSTR + col];
-        if constexpr (C::UQ == 4) {
-          u32x2 a, c;
-          a[0] = bf16_bits(qreg[0], e) | (bf16_bits(qreg[1], e) << 16);
-          a[1] = bf16_bits(qreg[2], e) | (bf16_bits(qreg[3], e) << 16);
-          c[0] = bf16_bits(oreg[0], e) | (bf16_bits(oreg[1], e) << 16);
-          c[1] = bf16_bits(oreg[2], e) | (bf16_bits(oreg[3], e) << 16);
-          *reinterpret_cast<u32x2*>(dq_) = a;
-          *reinterpret_cast<u32x2*>(do_) = c;
-        } else {
-          *reinterpret_cast<unsigned*>(dq_) = bf16_bits(qreg[0], e) | (bf16_bits(qreg[1], e) << 16);
-          *reinterpret_cast<unsigned*>(do_) = bf16_bits(oreg[0], e) | (bf16_bits(oreg[1], e) << 16);
-        }
-      }
-      if (tid < BQ) {
-        lse2s[tid] = lse_reg;
-        Ds[tid] = d_reg;
-      }
-    };
-
-    load_q(qb_start * BQ);
-    for (int qb = qb_start; qb < nqb; ++qb) {
-      const int q0 = qb * BQ;
-      store_q();
-      __syncthreads();
-      if (qb + 1 < nqb) load_q(q0 + BQ);
-
-      const bool active = (kw0 < kv_lim) && (!causal || q0 + BQ - 1 >= kw0);
-      if (active) {
-        // S = Q K^T and dP = dO V^T: rows = queries 32*qt + 8i + 4g + j, column = key.
-        f32x16 sa[BQ / 32], pa[BQ / 32];
-#pragma unroll
-        for (int qt = 0; qt < BQ / 32; ++qt)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            sa[qt][e] = 0.f;
-            pa[qt][e] = 0.f;
-          }
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk)
-#pragma unroll
-          for (int qt = 0; qt < BQ / 32; ++qt) {
-            sa[qt] = mfma32(ld_lds16(&Qs[(32 * qt + r) * C::QSTR + 16 * kk + 8 * g]), kf[kk], sa[qt]);
-            pa[qt] = mfma32(ld_lds16(&dOs[(32 * qt + r) * C::QSTR + 16 * kk + 8 * g]), vf[kk], pa[qt]);
-          }
-
-        const bool need_mask = (kw0 + 31 >= kv_lim) || (causal && q0 < kw0 + 31);
-#pragma unroll
-        for (int qt = 0; qt < BQ / 32; ++qt)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int ql = 32 * qt + 8 * (e >> 2) + 4 * g + (e & 3);
-            float p = fast_exp2(sa[qt][e] * sl2 - lse2s[ql]);
-            if (need_mask && (key >= kv_lim || (causal && key > q0 + ql))) p = 0.f;
-            sa[qt][e] = p;
-            pa[qt][e] = p * (pa[qt][e] - Ds[ql]);
-          }
-
-        bf16x8 pb[BQ / 16], db[BQ / 16], pl[PRECISE ? BQ / 16 : 1], dl[PRECISE ? BQ / 16 : 1];
-#pragma unroll
-        for (int c = 0; c < BQ / 16; ++c) {
-          if constexpr (PRECISE) {
-            pack_split_bf16x8(sa[c >> 1], 8 * (c & 1), pb[c], pl[c]);
-            pack_split_bf16x8(pa[c >> 1], 8 * (c & 1), db[c], dl[c]);
-          } else {
-            pb[c] = pack_bf16x8(sa[c >> 1], 8 * (c & 1));
-            db[c] = pack_bf16x8(pa[c >> 1], 8 * (c & 1));
-          }
-        }
-#pragma unroll
-        for (int t = 0; t < D / 32; ++t)
-#pragma unroll
-          for (int c = 0; c < BQ / 16; ++c) {
-            const bf16x8 aO = ld_lds16(&dOT[(32 * t + r) * C::TSTR + 16 * c + 8 * g]);
-            const bf16x8 aQ = ld_lds16(&QT[(32 * t + r) * C::TSTR + 16 * c + 8 * g]);
-            dv[t] = mfma32(aO, pb[c], dv[t]);
-            dk[t] = mfma32(aQ, db[c], dk[t]);
-            if constexpr (PRECISE) {
-              dv[t] = mfma32(aO, pl[c], dv[t]);
-              dk[t] = mfma32(aQ, dl[c], dk[t]);
-            }
-          }
-        // dS (bf16) into the row-major [query][key] tile for the dQ product.
-#pragma unroll
-        for (int part = 0; part < (PRECISE ? 2 : 1); ++part) {
-          u16* dst = dSs + part * BQ * C::DSSTR;
-#pragma unroll
-          for (int c = 0; c < BQ / 16; ++c) {
-            const u32x4 words = __builtin_bit_cast(u32x4, part == 0 ? db[c] : dl[PRECISE ? c : 0]);
-#pragma unroll
-            for (int s8 = 0; s8 < 8; ++s8) {
-              const int ql = 16 * c + 8 * (s8 >> 2) + 4 * g + (s8 & 3);
-              dst[ql * C::DSSTR + 32 * w + r] = (u16)(words[s8 >> 1] >> ((s8 & 1) * 16));
-            }
-          }
-        }
-      } else {
-        for (int idx = lane; idx < (PRECISE ? 2 : 1) * BQ * 4; idx += 64) {
-          const u32x4 z = {0u, 0u, 0u, 0u};
-          *reinterpret_cast<u32x4*>(&dSs[(idx >> 2) * C::DSSTR + 32 * w + 8 * (idx & 3)]) = z;
-        }
-      }
-      __syncthreads();
-
-      // dQ_i += s dS K over the workgroup's keys: tiles (qt, dt) of 32 x 32, split over waves.
-      constexpr int NT = (BQ / 32) * (D / 32);
-      for (int tt = w; tt < NT; tt += C::NW) {
-        const int qt = tt / (D / 32), dt = tt % (D / 32);
-        f32x16 acc;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[e] = 0.f;
-#pragma unroll
-        for (int c = 0; c < C::BKV / 16; ++c) {
-          const bf16x8 bK = ld_lds16(&KT[(32 * dt + r) * C::KTSTR + 16 * c + 8 * g]);
-          acc = mfma32(ld_lds16(&dSs[(32 * qt + r) * C::DSSTR + 16 * c + 8 * g]), bK, acc);
-          if constexpr (PRECISE)
-            acc = mfma32(ld_lds16(&dSs[(BQ + 32 * qt + r) * C::DSSTR + 16 * c + 8 * g]), bK, acc);
-        }
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int qq = q0 + 32 * qt + 8 * (e >> 2) + 4 * g + (e & 3);
-          if (qq < N) unsafeAtomicAdd(dQ + head + (size_t)qq * D + 32 * dt + r, acc[e] * scale);
-        }
-      }
-    }
-  }
-
-  if (key < N) {
-    float* dkrow = dK + head + (size_t)key * D;
-    float* dvrow = dV + head + (size_t)key * D;
-#pragma unroll
-    for (int t = 0; t < D / 32; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f32x4 a, c;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          a[j] = dk[t][4 * i + j] * scale;
-          c[j] = dv[t][4 * i + j];
-        }
-        *reinterpret_cast<f32x4*>(dkrow + 32 * t + 8 * i + 4 * g) = a;
-        *reinterpret_cast<f32x4*>(dvrow + 32 * t + 8 * i + 4 * g) = c;
-      }
-  }
-}
-
-// ---------------------------------------------------------------- split kernels
+// ---------------------------------------------------------------- key-outer kernel
 //
 // Default backward: two kernels that each write their outputs once, no
-// atomics. dK, dV come from a key-outer kernel; dQ from a query-outer kernel
-// shaped like the forward. Both recompute S and dP, so together they do 7 of
-// the 5 algorithmic matrix products' worth of work, in exchange for no dQ
-// accumulation traffic and no cross-workgroup dependency.
+// atomics. dK, dV come from the key-outer kernel below; dQ from a query-outer
+// kernel shaped like the forward. Both recompute S and dP, so together they
+// do 7 of the 5 algorithmic matrix products' worth of work, in exchange for
+// no dQ accumulation traffic and no cross-workgroup dependency.
+// FA_BWD_DQ_ATOMIC instead runs the key-outer kernel with DQ_ATOMIC set: it
+// also forms dQ_i += dS K for its keys and adds it into dQ with fp32 atomics.
 
 template <int D>
 struct DkdvCfg {
@@ -501,6 +225,8 @@ struct DkdvCfg {
   // measured faster (shorter sequences, lighter per-block products)
   static constexpr int BQ = D == 128 ? 64 : 32;
   static constexpr int CH = BQ * D / 8 / 256;  // 16-byte chunks per thread per tensor
+  static constexpr int KCH = BKV * D / 8 / 256;
+  static constexpr int DSTR = BKV + 8;         // dS tile row stride (row reads only)
   static_assert(CH >= 1, "one chunk per thread at least");
 };
 
@@ -509,18 +235,22 @@ struct DkdvCfg {
 // double-buffered LDS tiles that serve as A operands both row-wise
 // (S = Q K^T, dP = dO V^T) and transposed (dV^T = dO^T P, dK^T = Q^T dS,
 // through ds_read_b64_tr_b16), with P and dS taken from registers.
-template <int D, bool PRECISE>
+template <int D, bool PRECISE, bool DQ_ATOMIC>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
     const u16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dg,
-    float* __restrict__ dK, float* __restrict__ dV, int H, int N, float scale, float sl2, int causal,
-    const int32_t* __restrict__ kv_len, int nkb, int total) {
+    float* __restrict__ dQ, float* __restrict__ dK, float* __restrict__ dV, int H, int N, float scale,
+    float sl2, int causal, const int32_t* __restrict__ kv_len, int nkb, int total) {
   using C = DkdvCfg<D>;
   constexpr int BQ = C::BQ;
+  constexpr int NSPLIT = PRECISE ? 2 : 1;
   __shared__ __attribute__((aligned(16))) u16 Qs[2][BQ * D];
   __shared__ __attribute__((aligned(16))) u16 dOs[2][BQ * D];
   __shared__ __attribute__((aligned(16))) float lse2s[2][BQ];
   __shared__ __attribute__((aligned(16))) float Ds[2][BQ];
+  // dQ path only: the workgroup's K rows (swizzled) and the dS tile(s).
+  __shared__ __attribute__((aligned(16))) u16 Kt[DQ_ATOMIC ? C::BKV * D : 8];
+  __shared__ __attribute__((aligned(16))) u16 dSs[DQ_ATOMIC ? NSPLIT * BQ * C::DSTR : 8];
 
   const int tile = xcd_tile(blockIdx.x, total);
   const int kbi = tile % nkb;  // ascending: causal key blocks with the most rows first
@@ -560,6 +290,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       const unsigned off = (unsigned)(key * D + 16 * kk + 8 * g) * 2;
       kf[kk] = as_bf16x8(ld_buf16(rK, off));
       vf[kk] = as_bf16x8(ld_buf16(rV, off));
+    }
+    if constexpr (DQ_ATOMIC) {
+#pragma unroll
+      for (int rr = 0; rr < C::KCH; ++rr) {
+        const int c = tid + 256 * rr;
+        const int row = c / (D / 8), col = (c % (D / 8)) * 8;
+        *reinterpret_cast<u32x4*>(&Kt[swz_off<D>(row, col)]) =
+            ld_buf16(rK, (unsigned)((kb0 + row) * D + col) * 2);
+      }
     }
 
     const int nqb = (N + BQ - 1) / BQ;
@@ -677,6 +416,57 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
               dk[t] = mfma32(aQ, dl[c], dk[t]);
             }
           }
+        if constexpr (DQ_ATOMIC) {
+          // dS (bf16, and its low half in precise mode) into the [query][key]
+          // tile: slot s of chunk c is query 16c + 8(s/4) + 4g + s%4.
+#pragma unroll
+          for (int part = 0; part < NSPLIT; ++part) {
+            u16* dst = dSs + part * BQ * C::DSTR;
+#pragma unroll
+            for (int c = 0; c < BQ / 16; ++c) {
+              const u32x4 words = __builtin_bit_cast(u32x4, part == 0 ? db[c] : dl[PRECISE ? c : 0]);
+#pragma unroll
+              for (int s8 = 0; s8 < 8; ++s8) {
+                const int ql = 16 * c + 8 * (s8 >> 2) + 4 * g + (s8 & 3);
+                dst[ql * C::DSTR + 32 * w + r] = (u16)(words[s8 >> 1] >> ((s8 & 1) * 16));
+              }
+            }
+          }
+        }
+      } else if constexpr (DQ_ATOMIC) {
+        for (int idx = lane; idx < NSPLIT * BQ * 4; idx += 64) {
+          const u32x4 z = {0u, 0u, 0u, 0u};
+          *reinterpret_cast<u32x4*>(&dSs[(idx >> 2) * C::DSTR + 32 * w + 8 * (idx & 3)]) = z;
+        }
+      }
+
+      if constexpr (DQ_ATOMIC) {
+        __syncthreads();
+        // dQ_i += s dS K over the workgroup's keys: 32x32 tiles (qt, dt) split
+        // over the waves; A = dS rows, B = K^T read transposed from Kt with
+        // the natural key order (k-slots 16c + 8g + 0..7).
+        constexpr int NT = (BQ / 32) * (D / 32);
+        const int kt_row = 8 * g + ((lane & 15) >> 2);
+        for (int tt = w; tt < NT; tt += C::NW) {
+          const int qt = tt / (D / 32), dt = tt % (D / 32);
+          f32x16 acc;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+#pragma unroll
+          for (int c = 0; c < C::BKV / 16; ++c) {
+            const int r0 = 16 * c + kt_row, col = 32 * dt + tr_col;
+            const bf16x8 bK = join_tr(ld_lds_tr(&Kt[swz_off<D>(r0, col)]),
+                                      ld_lds_tr(&Kt[swz_off<D>(r0 + 4, col)]));
+#pragma unroll
+            for (int part = 0; part < NSPLIT; ++part)
+              acc = mfma32(ld_lds16(&dSs[(part * BQ + 32 * qt + r) * C::DSTR + 16 * c + 8 * g]), bK, acc);
+          }
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int qq = q0 + 32 * qt + 8 * (e >> 2) + 4 * g + (e & 3);
+            if (qq < N) unsafeAtomicAdd(dQ + head + (size_t)qq * D + 32 * dt + r, acc[e] * scale);
+          }
+        }
       }
       if (qb + 1 < nqb) store(buf ^ 1);
       __syncthreads();
@@ -869,6 +659,16 @@ __global__ __launch_bounds__(256, PRECISE ? 1 : 2) void bwd_dq_kernel(
   }
 }
 
+template <int D, bool PRECISE, bool DQ_ATOMIC>
+static void launch_dkdv(const u16* q, const u16* k, const u16* v, const u16* g, const float* LSE,
+                        const float* Dws, float* dQ, float* dK, float* dV, const AttnShape& s, float sl2,
+                        hipStream_t stream) {
+  const int nkb = (s.N + DkdvCfg<D>::BKV - 1) / DkdvCfg<D>::BKV;
+  const int total = s.B * s.H * nkb;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, PRECISE, DQ_ATOMIC>), dim3(total), dim3(256), 0, stream, q, k, v, g,
+                     LSE, Dws, dQ, dK, dV, s.H, s.N, s.scale, sl2, s.causal, s.kv_len, nkb, total);
+}
+
 template <int D>
 static hipError_t launch_bwd_d(const void* Q, const void* K, const void* V, const void* O,
                                const void* dO, const float* LSE, float* dQ, float* dK, float* dV,
@@ -898,28 +698,18 @@ static hipError_t launch_bwd_d(const void* Q, const void* K, const void* V, cons
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (dq_atomic) {
-    const int nkb = (s.N + BwdCfg<D>::BKV - 1) / BwdCfg<D>::BKV;
-    const int total = s.B * s.H * nkb;
     if (precise)
-      hipLaunchKernelGGL((bwd_bf16_kernel<D, true>), dim3(total), dim3(256), 0, stream, q, k, v, g, LSE,
-                         Dws, dQ, dK, dV, s.H, s.N, s.scale, sl2, s.causal, s.kv_len, nkb, total);
+      launch_dkdv<D, true, true>(q, k, v, g, LSE, Dws, dQ, dK, dV, s, sl2, stream);
     else
-      hipLaunchKernelGGL((bwd_bf16_kernel<D, false>), dim3(total), dim3(256), 0, stream, q, k, v, g, LSE,
-                         Dws, dQ, dK, dV, s.H, s.N, s.scale, sl2, s.causal, s.kv_len, nkb, total);
+      launch_dkdv<D, false, true>(q, k, v, g, LSE, Dws, dQ, dK, dV, s, sl2, stream);
     return hipGetLastError();
   }
-  {
-    const int nkb = (s.N + DkdvCfg<D>::BKV - 1) / DkdvCfg<D>::BKV;
-    const int total = s.B * s.H * nkb;
-    if (precise)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3(total), dim3(256), 0, stream, q, k, v, g, LSE,
-                         Dws, dK, dV, s.H, s.N, s.scale, sl2, s.causal, s.kv_len, nkb, total);
-    else
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3(total), dim3(256), 0, stream, q, k, v, g, LSE,
-                         Dws, dK, dV, s.H, s.N, s.scale, sl2, s.causal, s.kv_len, nkb, total);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
+  if (precise)
+    launch_dkdv<D, true, false>(q, k, v, g, LSE, Dws, dQ, dK, dV, s, sl2, stream);
+  else
+    launch_dkdv<D, false, false>(q, k, v, g, LSE, Dws, dQ, dK, dV, s, sl2, stream);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
   {
     const int nqb = (s.N + DqCfg<D>::BR - 1) / DqCfg<D>::BR;
     const int total = s.B * s.H * nqb;

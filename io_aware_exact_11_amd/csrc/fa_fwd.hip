@@ -162,6 +162,9 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   __syncthreads();
   f32x16 s_cur[BC / 32];
   if (nt_w > 0) qk(0, s_cur);
+  // K_0's buffer is refilled with K_2 during the first tile: every wave must
+  // have taken its scores from it first.
+  __syncthreads();
 
   for (int it = 0; it < nt; ++it) {
     const int kb = it * BC;
