@@ -303,8 +303,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 
     const int nqb = (N + BQ - 1) / BQ;
     const int qb_start = causal ? kb0 / BQ : 0;
+    // Row statistics of the head through buffer resources: raw loads only
+    // here, arithmetic at store time, so that nothing waits on the prefetch
+    // (memory counters retire in order) until the block is written to LDS.
+    const auto rL = make_rsrc(LSE + (size_t)bh * N, (unsigned)N * 4);
+    const auto rD = make_rsrc(Dg + (size_t)bh * N, (unsigned)N * 4);
     u32x4 qreg[C::CH], oreg[C::CH];
-    float lreg = 0.f, dreg = 0.f;
+    float lraw = 0.f, draw = 0.f;
+    int qrow = 0;
     auto load = [&](int q0) {
 #pragma unroll
       for (int rr = 0; rr < C::CH; ++rr) {
@@ -313,11 +319,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
         qreg[rr] = ld_buf16(rQ, off);
         oreg[rr] = ld_buf16(rO, off);
       }
-      if (tid < BQ) {
-        const int qq = q0 + tid;
-        lreg = qq < N ? LSE[(size_t)bh * N + qq] * kLog2e : INFINITY;
-        dreg = qq < N ? Dg[(size_t)bh * N + qq] : 0.f;
-      }
+      qrow = q0 + (tid & (BQ - 1));
+      lraw = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rL, (unsigned)qrow * 4, 0, 0));
+      draw = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rD, (unsigned)qrow * 4, 0, 0));
     };
     auto store = [&](int buf) {
 #pragma unroll
@@ -328,8 +332,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
         *reinterpret_cast<u32x4*>(&dOs[buf][off]) = oreg[rr];
       }
       if (tid < BQ) {
-        lse2s[buf][tid] = lreg;
-        Ds[buf][tid] = dreg;
+        // rows past N: weight 0 (LSE = +inf) and no D term
+        lse2s[buf][tid] = qrow < N ? lraw * kLog2e : INFINITY;
+        Ds[buf][tid] = qrow < N ? draw : 0.f;
       }
     };
     // Transposing-read coordinates of this lane (see ld_lds_tr): row part
@@ -497,15 +502,15 @@ struct DqCfg {
   static constexpr int NW = 4;
   static constexpr int BR = 32 * NW;           // query rows per workgroup
   static constexpr int BC = 64;                // keys per tile
-  static constexpr int VSTR = D + 8;           // padded V tile stride (row reads only)
-  static constexpr int CH = BC * D / 8 / 256;
 };
 
 // dQ for 128 query rows of one (b, h), written once. Shaped like the
 // forward: S^T = K Q^T and dP^T = V dO^T with the wave's Q and dO rows as B
 // operands, so each lane holds one query's P and dS for 32 keys of a tile;
 // dQ^T += K^T dS^T takes dS from those registers and K^T from the same
-// (swizzled) K tile through transposing reads.
+// (swizzled) K tile through transposing reads. K and V tiles arrive by
+// direct buffer-to-LDS loads, double-buffered, which keeps the kernel's
+// registers within two waves per SIMD without spilling.
 template <int D, bool PRECISE>
 __global__ __launch_bounds__(256, PRECISE ? 1 : 2) void bwd_dq_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
@@ -515,7 +520,7 @@ __global__ __launch_bounds__(256, PRECISE ? 1 : 2) void bwd_dq_kernel(
   using C = DqCfg<D>;
   constexpr int BC = C::BC;
   __shared__ __attribute__((aligned(16))) u16 Ks[2][BC * D];
-  __shared__ __attribute__((aligned(16))) u16 Vs[2][BC * C::VSTR];
+  __shared__ __attribute__((aligned(16))) u16 Vs[2][BC * D];
 
   const int tile = xcd_tile(blockIdx.x, total);
   int qb = tile % nqb;
@@ -560,48 +565,30 @@ __global__ __launch_bounds__(256, PRECISE ? 1 : 2) void bwd_dq_kernel(
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[t][e] = 0.f;
 
-  u32x4 kreg[C::CH], vreg[C::CH];
-  auto load = [&](int kb) {
-#pragma unroll
-    for (int rr = 0; rr < C::CH; ++rr) {
-      const int c = tid + 256 * rr;
-      const unsigned off = (unsigned)((kb + c / (D / 8)) * D + (c % (D / 8)) * 8) * 2;
-      kreg[rr] = ld_buf16(rK, off);
-      vreg[rr] = ld_buf16(rV, off);
-    }
-  };
-  auto store = [&](int buf) {
-#pragma unroll
-    for (int rr = 0; rr < C::CH; ++rr) {
-      const int c = tid + 256 * rr;
-      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-      *reinterpret_cast<u32x4*>(&Ks[buf][swz_off<D>(row, col)]) = kreg[rr];
-      *reinterpret_cast<u32x4*>(&Vs[buf][row * C::VSTR + col]) = vreg[rr];
-    }
+  auto load = [&](int kb, int buf) {
+    tile_to_lds<D, BC, C::NW>(rK, kb, Ks[buf], w, lane);
+    tile_to_lds<D, BC, C::NW>(rV, kb, Vs[buf], w, lane);
   };
   const int tr_row = 4 * g + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
-  if (nt > 0) {
-    load(0);
-    store(0);
-  }
+  if (nt > 0) load(0, 0);
   __syncthreads();
   for (int it = 0; it < nt; ++it) {
     const int buf = it & 1;
     const int kb = it * BC;
-    if (it + 1 < nt) load(kb + BC);
+    if (it + 1 < nt) load(kb + BC, buf ^ 1);
     if (it < nt_w) {
       f32x16 s[BC / 32], dp[BC / 32];
 #pragma unroll
       for (int mt = 0; mt < BC / 32; ++mt) {
         const int row = 32 * mt + r;
         s[mt] = mfma32_first(ld_lds16(&Ks[buf][swz_off<D>(row, 8 * g)]), qf[0]);
-        dp[mt] = mfma32_first(ld_lds16(&Vs[buf][row * C::VSTR + 8 * g]), df[0]);
+        dp[mt] = mfma32_first(ld_lds16(&Vs[buf][swz_off<D>(row, 8 * g)]), df[0]);
 #pragma unroll
         for (int kk = 1; kk < D / 16; ++kk) {
           s[mt] = mfma32(ld_lds16(&Ks[buf][swz_off<D>(row, 16 * kk + 8 * g)]), qf[kk], s[mt]);
-          dp[mt] = mfma32(ld_lds16(&Vs[buf][row * C::VSTR + 16 * kk + 8 * g]), df[kk], dp[mt]);
+          dp[mt] = mfma32(ld_lds16(&Vs[buf][swz_off<D>(row, 16 * kk + 8 * g)]), df[kk], dp[mt]);
         }
       }
       if ((kb + BC > kv_lim) || (causal && kb + BC - 1 > wave_q_first)) {
@@ -641,7 +628,6 @@ __global__ __launch_bounds__(256, PRECISE ? 1 : 2) void bwd_dq_kernel(
           if constexpr (PRECISE) acc[t] = mfma32(aK, dl[c], acc[t]);
         }
     }
-    if (it + 1 < nt) store(buf ^ 1);
     __syncthreads();
   }
 

@@ -132,6 +132,29 @@ __device__ __forceinline__ int swz_off(int r, int col) {
   return r * D + ((((col >> 3) ^ swz<D>(r)) << 3) | (col & 7));
 }
 
+// Load a ROWS x D bf16 tile (global rows row0.., row stride D) into a
+// swizzled LDS tile with direct buffer-to-LDS loads: no registers are
+// staged. Each wave instruction moves 1 KB, lane l landing at byte 16 l of
+// it; the lane therefore fetches the global chunk that the swizzle places
+// there. Rows past the end of the buffer read as zeros (out-of-range lanes
+// of a buffer-to-LDS load write zeros). The data is visible to the other
+// waves after the next barrier, which waits for these loads.
+template <int D, int ROWS, int NW>
+__device__ __forceinline__ void tile_to_lds(__amdgpu_buffer_rsrc_t rs, int row0, u16* tile, int w,
+                                            int lane) {
+  constexpr int INST = ROWS * D * 2 / 1024;
+  static_assert(INST % NW == 0, "whole 1 KB blocks per wave");
+#pragma unroll
+  for (int i = 0; i < INST / NW; ++i) {
+    const int blk = w * (INST / NW) + i;
+    const int e0 = blk * 512 + lane * 8;
+    const int row = e0 / D, pc = (e0 % D) >> 3;
+    const unsigned goff = (unsigned)((row0 + row) * D + ((pc ^ swz<D>(row)) << 3)) * 2;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (__attribute__((address_space(3))) void*)(tile + blk * 512), 16, (int)goff, 0, 0, 0);
+  }
+}
+
 // Map a linear workgroup id to a tile id so that the tiles of one (b, h)
 // run on one XCD, in order: workgroups are dispatched round-robin over the
 // 8 XCDs, each with its own L2, and neighbouring tiles of a head share K, V.
