@@ -4,7 +4,7 @@
 
 Prints one JSON line. The step runs the library's whole path on inputs that
 are already resident in device memory: flash_attn_fwd (O, LSE) then
-flash_attn_bwd (dQ zero-fill, D pre-pass, main backward kernel). FLOPs are
+flash_attn_bwd (D pre-pass, key-outer dK/dV kernel, query-outer dQ kernel). FLOPs are
 counted over visible (query, key) pairs only: 4 d per pair forward (the two
 products S = Q K^T and O = P V at 2 flops per multiply-add) and 10 d per
 pair backward (recomputed S, dP, dV, dK, dQ), 14 d per pair for a step.
@@ -231,7 +231,7 @@ def main():
         "fwd_tflops": round(ff / (fwd_ms * 1e-3) / 1e12, 2),
         "fwd_ms": round(fwd_ms, 4),
         "bwd_ms": round(bwd_ms, 4),
-        "roofline": {"kernel": "flash_attn_bwd call (dQ fill + D pre-pass + main kernel)",
+        "roofline": {"kernel": "flash_attn_bwd call (D pre-pass + dK/dV kernel + dQ kernel)",
                      "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic},
