@@ -1,0 +1,687 @@
+// Backward pass of exact attention for gfx950: bf16 inputs, fp32 gradients.
+//
+// The forward kept only O and one log-sum-exp per row; here the score and
+// probability tiles are rebuilt block by block from Q, K, V
+// ("FlashAttention and GPU Memory", chapter 09 Backward: recomputing beats
+// reading; "FlashAttention does more arithmetic to move less data", move 4).
+// With P_ij = exp(s q_i.k_j - LSE_i) the gradients are, by the chain rule,
+//   dV = P^T dO,  dP = dO V^T,  dS = P o (dP - D),  dK = s dS^T Q,  dQ = s dS K,
+// where D_i = sum_j P_ij dP_ij. Since O = P V, D_i equals dO_i . O_i, which a
+// bandwidth-bound pre-pass computes from O and dO (default), or, with
+// FA_BWD_PRECISE, a separate recompute pass sums P o dP exactly.
+//
+// Main kernel (one workgroup per 128 keys of one (b, h), 4 waves of 32 keys):
+//   * the wave's K and V rows sit in registers as the B operands of
+//     S = Q K^T and dP = dO V^T (32x32x16 bf16 products, fp32 accumulate);
+//   * query blocks of 64 rows stream through LDS, stored both row-major
+//     (A operand of S and dP) and transposed (A operand of dV^T = dO^T P and
+//     dK^T = Q^T dS, whose B operands are the P and dS registers themselves);
+//   * dV^T and dK^T for the wave's keys accumulate in registers across all
+//     query blocks and are written once;
+//   * dS goes to LDS, and the workgroup adds dQ_i += s dS K for its 128 keys
+//     into the fp32 dQ output with hardware float atomics.
+// Causal workgroups start at the first query block that can see their keys;
+// waves whose keys are all invisible to a block skip its products.
+#pragma once
+
+#include "fa_common.h"
+#include "fa_launch.h"
+
+namespace fa {
+
+// D_i = sum_c dO[i,c] * O[i,c] in fp32 from the bf16 tensors; 16 lanes per row.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dot_kernel(const u16* __restrict__ O,
+                                                      const u16* __restrict__ dO,
+                                                      float* __restrict__ Dout, int rows) {
+  constexpr int EPL = D / 16;  // elements per lane: 8 or 4
+  const int gid = blockIdx.x * 256 + threadIdx.x;
+  const int row = gid >> 4, sub = gid & 15;
+  float acc = 0.f;
+  if (row < rows) {
+    const size_t off = (size_t)row * D + sub * EPL;
+    if constexpr (EPL == 8) {
+      const u32x4 a = ld_global16(O + off), c = ld_global16(dO + off);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        acc += __uint_as_float(bf16_bits(a, e) << 16) * __uint_as_float(bf16_bits(c, e) << 16);
+    } else {
+      const u32x2 a = *reinterpret_cast<const u32x2*>(O + off);
+      const u32x2 c = *reinterpret_cast<const u32x2*>(dO + off);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const unsigned ab = (a[e >> 1] >> ((e & 1) * 16)) & 0xffffu;
+        const unsigned cb = (c[e >> 1] >> ((e & 1) * 16)) & 0xffffu;
+        acc += __uint_as_float(ab << 16) * __uint_as_float(cb << 16);
+      }
+    }
+  }
+  acc += __shfl_xor(acc, 8);
+  acc += __shfl_xor(acc, 4);
+  acc += __shfl_xor(acc, 2);
+  acc += __shfl_xor(acc, 1);
+  if (row < rows && sub == 0) Dout[row] = acc;
+}
+
+// D_i = sum_j P_ij dP_ij taken literally, for FA_BWD_PRECISE: a query-outer
+// pass (one workgroup per 128 query rows, 32 per wave) that recomputes the
+// score tile S^T = K Q^T and dP^T = V dO^T on the matrix cores, with both K
+// and V tiles streamed row-major through double-buffered LDS and the wave's
+// Q and dO rows held as B operands; P_ij = 2^(s_ij*scale*log2e - LSE_i*log2e)
+// uses the saved LSE. Independent of O, so the bf16 rounding of O does not
+// enter D.
+template <int D>
+struct ExactDCfg {
+  static constexpr int BR = 128;
+  static constexpr int BC = 64;
+  static constexpr int KSTR = D + 8;
+  static constexpr int KCH = BC * D / 8 / 256;
+};
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void bwd_exact_d_kernel(
+    const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
+    const u16* __restrict__ dO, const float* __restrict__ LSE, float* __restrict__ Dout, int H,
+    int N, float sl2, int causal, const int32_t* __restrict__ kv_len, int nqb, int total) {
+  using C = ExactDCfg<D>;
+  constexpr int BC = C::BC;
+  __shared__ __attribute__((aligned(16))) u16 Ks[2][BC * C::KSTR];
+  __shared__ __attribute__((aligned(16))) u16 Vs[2][BC * C::KSTR];
+
+  const int tile = xcd_tile(blockIdx.x, total);
+  int qb = tile % nqb;
+  const int bh = tile / nqb;
+  if (causal) qb = nqb - 1 - qb;
+  const int b = bh / H;
+  const int q0 = qb * C::BR;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, r = lane & 31, g = lane >> 5;
+  const size_t head = (size_t)bh * N * D;
+
+  int kv_lim = N;
+  if (kv_len) {
+    const int L = kv_len[b];
+    kv_lim = L < 0 ? 0 : (L > N ? N : L);
+  }
+  int kv_end = kv_lim;
+  if (causal) kv_end = min(kv_end, q0 + C::BR);
+  const int nt = (kv_end + BC - 1) / BC;
+
+  const int q = q0 + 32 * w + r;
+  const int wave_q_first = q0 + 32 * w, wave_q_last = wave_q_first + 31;
+  bf16x8 qf[D / 16], df[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    u32x4 a = {0u, 0u, 0u, 0u}, c = {0u, 0u, 0u, 0u};
+    if (q < N) {
+      a = ld_global16(Q + head + (size_t)q * D + 16 * kk + 8 * g);
+      c = ld_global16(dO + head + (size_t)q * D + 16 * kk + 8 * g);
+    }
+    qf[kk] = as_bf16x8(a);
+    df[kk] = as_bf16x8(c);
+  }
+  const float lse2 = q < N ? LSE[(size_t)bh * N + q] * kLog2e : INFINITY;
+  float part = 0.f;
+
+  u32x4 kreg[C::KCH], vreg[C::KCH];
+  auto load_tile = [&](int kb) {
+#pragma unroll
+    for (int rr = 0; rr < C::KCH; ++rr) {
+      const int c = tid + 256 * rr;
+      const int key = kb + c / (D / 8);
+      u32x4 a = {0u, 0u, 0u, 0u}, v = {0u, 0u, 0u, 0u};
+      if (key < N) {
+        a = ld_global16(K + head + (size_t)key * D + (c % (D / 8)) * 8);
+        v = ld_global16(V + head + (size_t)key * D + (c % (D / 8)) * 8);
+      }
+      kreg[rr] = a;
+      vreg[rr] = v;
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int rr = 0; rr < C::KCH; ++rr) {
+      const int c = tid + 256 * rr;
+      const int off = (c / (D / 8)) * C::KSTR + (c % (D / 8)) * 8;
+      *reinterpret_cast<u32x4*>(&Ks[buf][off]) = kreg[rr];
+      *reinterpret_cast<u32x4*>(&Vs[buf][off]) = vreg[rr];
+    }
+  };
+
+  if (nt > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+  for (int it = 0; it < nt; ++it) {
+    const int buf = it & 1;
+    const int kb = it * BC;
+    if (it + 1 < nt) load_tile(kb + BC);
+    if (!causal || kb <= wave_q_last) {
+      f32x16 s[BC / 32], dp[BC / 32];
+#pragma unroll
+      for (int mt = 0; mt < BC / 32; ++mt) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          s[mt][e] = 0.f;
+          dp[mt][e] = 0.f;
+        }
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+          const int off = (32 * mt + r) * C::KSTR + 16 * kk + 8 * g;
+          s[mt] = mfma32(ld_lds16(&Ks[buf][off]), qf[kk], s[mt]);
+          dp[mt] = mfma32(ld_lds16(&Vs[buf][off]), df[kk], dp[mt]);
+        }
+      }
+      const bool need_mask = (kb + BC > kv_lim) || (causal && kb + BC - 1 > wave_q_first);
+#pragma unroll
+      for (int mt = 0; mt < BC / 32; ++mt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = kb + 32 * mt + 8 * (e >> 2) + 4 * g + (e & 3);
+          float p = fast_exp2(s[mt][e] * sl2 - lse2);
+          if (need_mask && (key >= kv_lim || (causal && key > q))) p = 0.f;
+          part += p * dp[mt][e];
+        }
+    }
+    if (it + 1 < nt) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+  part += __shfl_xor(part, 32);
+  if (q < N && g == 0) Dout[(size_t)bh * N + q] = part;
+}
+
+// ---------------------------------------------------------------- key-outer kernel
+//
+// Default backward: two kernels that each write their outputs once, no
+// atomics. dK, dV come from the key-outer kernel below; dQ from a query-outer
+// kernel shaped like the forward. Both recompute S and dP, so together they
+// do 7 of the 5 algorithmic matrix products' worth of work, in exchange for
+// no dQ accumulation traffic and no cross-workgroup dependency.
+// FA_BWD_DQ_ATOMIC instead runs the key-outer kernel with DQ_ATOMIC set: it
+// also forms dQ_i += dS K for its keys and adds it into dQ with fp32 atomics.
+
+template <int D>
+struct DkdvCfg {
+  static constexpr int NW = 4;
+  static constexpr int BKV = 32 * NW;          // keys per workgroup (32 per wave)
+  // query rows per block: 64 at d=128; 32 at d=64, where the smaller blocks
+  // measured faster (shorter sequences, lighter per-block products)
+  static constexpr int BQ = D == 128 ? 64 : 32;
+  static constexpr int CH = BQ * D / 8 / 256;  // 16-byte chunks per thread per tensor
+  static constexpr int KCH = BKV * D / 8 / 256;
+  static constexpr int DSTR = BKV + 8;         // dS tile row stride (row reads only)
+  static_assert(CH >= 1, "one chunk per thread at least");
+};
+
+// dK, dV for 128 keys of one (b, h). The wave's K and V rows are B operands
+// held in registers; query blocks of Q and dO stream through swizzled,
+// double-buffered LDS tiles that serve as A operands both row-wise
+// (S = Q K^T, dP = dO V^T) and transposed (dV^T = dO^T P, dK^T = Q^T dS,
+// through ds_read_b64_tr_b16), with P and dS taken from registers.
+template <int D, bool PRECISE, bool DQ_ATOMIC>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
+    const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
+    const u16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dg,
+    float* __restrict__ dQ, float* __restrict__ dK, float* __restrict__ dV, int H, int N, float scale,
+    float sl2, int causal, const int32_t* __restrict__ kv_len, int nkb, int total) {
+  using C = DkdvCfg<D>;
+  constexpr int BQ = C::BQ;
+  constexpr int NSPLIT = PRECISE ? 2 : 1;
+  __shared__ __attribute__((aligned(16))) u16 Qs[2][BQ * D];
+  __shared__ __attribute__((aligned(16))) u16 dOs[2][BQ * D];
+  __shared__ __attribute__((aligned(16))) float lse2s[2][BQ];
+  __shared__ __attribute__((aligned(16))) float Ds[2][BQ];
+  // dQ path only: the workgroup's K rows (swizzled) and the dS tile(s).
+  __shared__ __attribute__((aligned(16))) u16 Kt[DQ_ATOMIC ? C::BKV * D : 8];
+  __shared__ __attribute__((aligned(16))) u16 dSs[DQ_ATOMIC ? NSPLIT * BQ * C::DSTR : 8];
+
+  const int tile = xcd_tile(blockIdx.x, total);
+  const int kbi = tile % nkb;  // ascending: causal key blocks with the most rows first
+  const int bh = tile / nkb;
+  const int b = bh / H;
+  const int kb0 = kbi * C::BKV;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, r = lane & 31, g = lane >> 5;
+  const int kw0 = kb0 + 32 * w;
+  const int key = kw0 + r;
+  const size_t head = (size_t)bh * N * D;
+  const unsigned head_bytes = (unsigned)N * D * 2;
+
+  int kv_lim = N;
+  if (kv_len) {
+    const int L = kv_len[b];
+    kv_lim = L < 0 ? 0 : (L > N ? N : L);
+  }
+
+  f32x16 dv[D / 32], dk[D / 32];
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      dv[t][e] = 0.f;
+      dk[t][e] = 0.f;
+    }
+
+  if (kb0 < kv_lim) {
+    const auto rQ = make_rsrc(Q + head, head_bytes);
+    const auto rK = make_rsrc(K + head, head_bytes);
+    const auto rV = make_rsrc(V + head, head_bytes);
+    const auto rO = make_rsrc(dO + head, head_bytes);
+    bf16x8 kf[D / 16], vf[D / 16];
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const unsigned off = (unsigned)(key * D + 16 * kk + 8 * g) * 2;
+      kf[kk] = as_bf16x8(ld_buf16(rK, off));
+      vf[kk] = as_bf16x8(ld_buf16(rV, off));
+    }
+    if constexpr (DQ_ATOMIC) {
+#pragma unroll
+      for (int rr = 0; rr < C::KCH; ++rr) {
+        const int c = tid + 256 * rr;
+        const int row = c / (D / 8), col = (c % (D / 8)) * 8;
+        *reinterpret_cast<u32x4*>(&Kt[swz_off<D>(row, col)]) =
+            ld_buf16(rK, (unsigned)((kb0 + row) * D + col) * 2);
+      }
+    }
+
+    const int nqb = (N + BQ - 1) / BQ;
+    const int qb_start = causal ? kb0 / BQ : 0;
+    // Row statistics of the head through buffer resources: raw loads only
+    // here, arithmetic at store time, so that nothing waits on the prefetch
+    // (memory counters retire in order) until the block is written to LDS.
+    const auto rL = make_rsrc(LSE + (size_t)bh * N, (unsigned)N * 4);
+    const auto rD = make_rsrc(Dg + (size_t)bh * N, (unsigned)N * 4);
+    u32x4 qreg[C::CH], oreg[C::CH];
+    float lraw = 0.f, draw = 0.f;
+    int qrow = 0;
+    auto load = [&](int q0) {
+#pragma unroll
+      for (int rr = 0; rr < C::CH; ++rr) {
+        const int c = tid + 256 * rr;
+        const unsigned off = (unsigned)((q0 + c / (D / 8)) * D + (c % (D / 8)) * 8) * 2;
+        qreg[rr] = ld_buf16(rQ, off);
+        oreg[rr] = ld_buf16(rO, off);
+      }
+      qrow = q0 + (tid & (BQ - 1));
+      lraw = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rL, (unsigned)qrow * 4, 0, 0));
+      draw = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rD, (unsigned)qrow * 4, 0, 0));
+    };
+    auto store = [&](int buf) {
+#pragma unroll
+      for (int rr = 0; rr < C::CH; ++rr) {
+        const int c = tid + 256 * rr;
+        const int off = swz_off<D>(c / (D / 8), (c % (D / 8)) * 8);
+        *reinterpret_cast<u32x4*>(&Qs[buf][off]) = qreg[rr];
+        *reinterpret_cast<u32x4*>(&dOs[buf][off]) = oreg[rr];
+      }
+      if (tid < BQ) {
+        // rows past N: weight 0 (LSE = +inf) and no D term
+        lse2s[buf][tid] = qrow < N ? lraw * kLog2e : INFINITY;
+        Ds[buf][tid] = qrow < N ? draw : 0.f;
+      }
+    };
+    // Transposing-read coordinates of this lane (see ld_lds_tr): row part
+    // 4g + (lane % 16) / 4 inside a 16-row chunk, column part
+    // 16 * ((lane / 16) % 2) + 4 * (lane % 4) inside a 32-column tile.
+    const int tr_row = 4 * g + ((lane & 15) >> 2);
+    const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+    load(qb_start * BQ);
+    store(0);
+    __syncthreads();
+    for (int qb = qb_start; qb < nqb; ++qb) {
+      const int q0 = qb * BQ;
+      const int buf = (qb - qb_start) & 1;
+      if (qb + 1 < nqb) load(q0 + BQ);
+
+      if ((kw0 < kv_lim) && (!causal || q0 + BQ - 1 >= kw0)) {
+        // S = Q K^T, dP = dO V^T: rows = queries 32*qt + 8i + 4g + j, column = key.
+        f32x16 sa[BQ / 32], pa[BQ / 32];
+#pragma unroll
+        for (int qt = 0; qt < BQ / 32; ++qt) {
+          const int row = 32 * qt + r;
+          sa[qt] = mfma32_first(ld_lds16(&Qs[buf][swz_off<D>(row, 8 * g)]), kf[0]);
+          pa[qt] = mfma32_first(ld_lds16(&dOs[buf][swz_off<D>(row, 8 * g)]), vf[0]);
+#pragma unroll
+          for (int kk = 1; kk < D / 16; ++kk) {
+            sa[qt] = mfma32(ld_lds16(&Qs[buf][swz_off<D>(row, 16 * kk + 8 * g)]), kf[kk], sa[qt]);
+            pa[qt] = mfma32(ld_lds16(&dOs[buf][swz_off<D>(row, 16 * kk + 8 * g)]), vf[kk], pa[qt]);
+          }
+        }
+        // Masked scores become -inf, so their weights come out exactly 0.
+        if ((kw0 + 31 >= kv_lim) || (causal && q0 < kw0 + 31)) {
+#pragma unroll
+          for (int qt = 0; qt < BQ / 32; ++qt)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const int qq = q0 + 32 * qt + 8 * (e >> 2) + 4 * g + (e & 3);
+              const bool off = (key >= kv_lim) | ((causal != 0) & (key > qq));
+              sa[qt][e] = off ? -INFINITY : sa[qt][e];
+            }
+        }
+#pragma unroll
+        for (int qt = 0; qt < BQ / 32; ++qt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int ql = 32 * qt + 8 * i + 4 * g;
+            const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse2s[buf][ql]);
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(&Ds[buf][ql]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int e = 4 * i + j;
+              const float p = fast_exp2(sa[qt][e] * sl2 - l4[j]);
+              sa[qt][e] = p;
+              pa[qt][e] = p * (pa[qt][e] - d4[j]);
+            }
+          }
+        bf16x8 pb[BQ / 16], db[BQ / 16], pl[PRECISE ? BQ / 16 : 1], dl[PRECISE ? BQ / 16 : 1];
+#pragma unroll
+        for (int c = 0; c < BQ / 16; ++c) {
+          if constexpr (PRECISE) {
+            pack_split_bf16x8(sa[c >> 1], 8 * (c & 1), pb[c], pl[c]);
+            pack_split_bf16x8(pa[c >> 1], 8 * (c & 1), db[c], dl[c]);
+          } else {
+            pb[c] = pack_bf16x8(sa[c >> 1], 8 * (c & 1));
+            db[c] = pack_bf16x8(pa[c >> 1], 8 * (c & 1));
+          }
+        }
+        // dV^T += dO^T P and dK^T += Q^T dS: A = the transposed tile (rows d =
+        // 32t + r, k-slots = queries 16c + 8h + 4g + 0..3 for slots 4h..4h+3),
+        // B = P / dS registers in the same slot order.
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+          for (int c = 0; c < BQ / 16; ++c) {
+            const int r0 = 16 * c + tr_row, col = 32 * t + tr_col;
+            const bf16x8 aO = join_tr(ld_lds_tr(&dOs[buf][swz_off<D>(r0, col)]),
+                                      ld_lds_tr(&dOs[buf][swz_off<D>(r0 + 8, col)]));
+            const bf16x8 aQ = join_tr(ld_lds_tr(&Qs[buf][swz_off<D>(r0, col)]),
+                                      ld_lds_tr(&Qs[buf][swz_off<D>(r0 + 8, col)]));
+            dv[t] = mfma32(aO, pb[c], dv[t]);
+            dk[t] = mfma32(aQ, db[c], dk[t]);
+            if constexpr (PRECISE) {
+              dv[t] = mfma32(aO, pl[c], dv[t]);
+              dk[t] = mfma32(aQ, dl[c], dk[t]);
+            }
+          }
+        if constexpr (DQ_ATOMIC) {
+          // dS (bf16, and its low half in precise mode) into the [query][key]
+          // tile: slot s of chunk c is query 16c + 8(s/4) + 4g + s%4.
+#pragma unroll
+          for (int part = 0; part < NSPLIT; ++part) {
+            u16* dst = dSs + part * BQ * C::DSTR;
+#pragma unroll
+            for (int c = 0; c < BQ / 16; ++c) {
+              const u32x4 words = __builtin_bit_cast(u32x4, part == 0 ? db[c] : dl[PRECISE ? c : 0]);
+#pragma unroll
+              for (int s8 = 0; s8 < 8; ++s8) {
+                const int ql = 16 * c + 8 * (s8 >> 2) + 4 * g + (s8 & 3);
+                dst[ql * C::DSTR + 32 * w + r] = (u16)(words[s8 >> 1] >> ((s8 & 1) * 16));
+              }
+            }
+          }
+        }
+      } else if constexpr (DQ_ATOMIC) {
+        for (int idx = lane; idx < NSPLIT * BQ * 4; idx += 64) {
+          const u32x4 z = {0u, 0u, 0u, 0u};
+          *reinterpret_cast<u32x4*>(&dSs[(idx >> 2) * C::DSTR + 32 * w + 8 * (idx & 3)]) = z;
+        }
+      }
+
+      if constexpr (DQ_ATOMIC) {
+        __syncthreads();
+        // dQ_i += s dS K over the workgroup's keys: 32x32 tiles (qt, dt) split
+        // over the waves; A = dS rows, B = K^T read transposed from Kt with
+        // the natural key order (k-slots 16c + 8g + 0..7).
+        constexpr int NT = (BQ / 32) * (D / 32);
+        const int kt_row = 8 * g + ((lane & 15) >> 2);
+        for (int tt = w; tt < NT; tt += C::NW) {
+          const int qt = tt / (D / 32), dt = tt % (D / 32);
+          f32x16 acc;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+#pragma unroll
+          for (int c = 0; c < C::BKV / 16; ++c) {
+            const int r0 = 16 * c + kt_row, col = 32 * dt + tr_col;
+            const bf16x8 bK = join_tr(ld_lds_tr(&Kt[swz_off<D>(r0, col)]),
+                                      ld_lds_tr(&Kt[swz_off<D>(r0 + 4, col)]));
+#pragma unroll
+            for (int part = 0; part < NSPLIT; ++part)
+              acc = mfma32(ld_lds16(&dSs[(part * BQ + 32 * qt + r) * C::DSTR + 16 * c + 8 * g]), bK, acc);
+          }
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int qq = q0 + 32 * qt + 8 * (e >> 2) + 4 * g + (e & 3);
+            if (qq < N) unsafeAtomicAdd(dQ + head + (size_t)qq * D + 32 * dt + r, acc[e] * scale);
+          }
+        }
+      }
+      if (qb + 1 < nqb) store(buf ^ 1);
+      __syncthreads();
+    }
+  }
+
+  if (key < N) {
+    float* dkrow = dK + head + (size_t)key * D;
+    float* dvrow = dV + head + (size_t)key * D;
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f32x4 a, c;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          a[j] = dk[t][4 * i + j] * scale;
+          c[j] = dv[t][4 * i + j];
+        }
+        *reinterpret_cast<f32x4*>(dkrow + 32 * t + 8 * i + 4 * g) = a;
+        *reinterpret_cast<f32x4*>(dvrow + 32 * t + 8 * i + 4 * g) = c;
+      }
+  }
+}
+
+template <int D>
+struct DqCfg {
+  static constexpr int NW = 4;
+  static constexpr int BR = 32 * NW;           // query rows per workgroup
+  static constexpr int BC = 64;                // keys per tile
+};
+
+// dQ for 128 query rows of one (b, h), written once. Shaped like the
+// forward: S^T = K Q^T and dP^T = V dO^T with the wave's Q and dO rows as B
+// operands, so each lane holds one query's P and dS for 32 keys of a tile;
+// dQ^T += K^T dS^T takes dS from those registers and K^T from the same
+// (swizzled) K tile through transposing reads. K and V tiles arrive by
+// direct buffer-to-LDS loads, double-buffered, which keeps the kernel's
+// registers within two waves per SIMD without spilling.
+template <int D, bool PRECISE>
+__global__ __launch_bounds__(256, PRECISE ? 1 : 2) void bwd_dq_kernel(
+    const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
+    const u16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dg,
+    float* __restrict__ dQ, int H, int N, float scale, float sl2, int causal,
+    const int32_t* __restrict__ kv_len, int nqb, int total) {
+  using C = DqCfg<D>;
+  constexpr int BC = C::BC;
+  __shared__ __attribute__((aligned(16))) u16 Ks[2][BC * D];
+  __shared__ __attribute__((aligned(16))) u16 Vs[2][BC * D];
+
+  const int tile = xcd_tile(blockIdx.x, total);
+  int qb = tile % nqb;
+  const int bh = tile / nqb;
+  if (causal) qb = nqb - 1 - qb;
+  const int b = bh / H;
+  const int q0 = qb * C::BR;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, r = lane & 31, g = lane >> 5;
+  const size_t head = (size_t)bh * N * D;
+  const unsigned head_bytes = (unsigned)N * D * 2;
+  const auto rQ = make_rsrc(Q + head, head_bytes);
+  const auto rK = make_rsrc(K + head, head_bytes);
+  const auto rV = make_rsrc(V + head, head_bytes);
+  const auto rO = make_rsrc(dO + head, head_bytes);
+
+  int kv_lim = N;
+  if (kv_len) {
+    const int L = kv_len[b];
+    kv_lim = L < 0 ? 0 : (L > N ? N : L);
+  }
+  int kv_end = kv_lim;
+  if (causal) kv_end = min(kv_end, q0 + C::BR);
+  const int nt = (kv_end + BC - 1) / BC;
+  const int q = q0 + 32 * w + r;
+  const int wave_q_first = q0 + 32 * w, wave_q_last = wave_q_first + 31;
+  const int nt_w = causal ? min(nt, wave_q_last / BC + 1) : nt;
+
+  bf16x8 qf[D / 16], df[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    const unsigned off = (unsigned)(q * D + 16 * kk + 8 * g) * 2;
+    qf[kk] = as_bf16x8(ld_buf16(rQ, off));
+    df[kk] = as_bf16x8(ld_buf16(rO, off));
+  }
+  const float lse2 = q < N ? LSE[(size_t)bh * N + q] * kLog2e : INFINITY;
+  const float Dq = q < N ? Dg[(size_t)bh * N + q] : 0.f;
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[t][e] = 0.f;
+
+  auto load = [&](int kb, int buf) {
+    tile_to_lds<D, BC, C::NW>(rK, kb, Ks[buf], w, lane);
+    tile_to_lds<D, BC, C::NW>(rV, kb, Vs[buf], w, lane);
+  };
+  const int tr_row = 4 * g + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+  if (nt > 0) load(0, 0);
+  __syncthreads();
+  for (int it = 0; it < nt; ++it) {
+    const int buf = it & 1;
+    const int kb = it * BC;
+    if (it + 1 < nt) load(kb + BC, buf ^ 1);
+    if (it < nt_w) {
+      f32x16 s[BC / 32], dp[BC / 32];
+#pragma unroll
+      for (int mt = 0; mt < BC / 32; ++mt) {
+        const int row = 32 * mt + r;
+        s[mt] = mfma32_first(ld_lds16(&Ks[buf][swz_off<D>(row, 8 * g)]), qf[0]);
+        dp[mt] = mfma32_first(ld_lds16(&Vs[buf][swz_off<D>(row, 8 * g)]), df[0]);
+#pragma unroll
+        for (int kk = 1; kk < D / 16; ++kk) {
+          s[mt] = mfma32(ld_lds16(&Ks[buf][swz_off<D>(row, 16 * kk + 8 * g)]), qf[kk], s[mt]);
+          dp[mt] = mfma32(ld_lds16(&Vs[buf][swz_off<D>(row, 16 * kk + 8 * g)]), df[kk], dp[mt]);
+        }
+      }
+      if ((kb + BC > kv_lim) || (causal && kb + BC - 1 > wave_q_first)) {
+#pragma unroll
+        for (int mt = 0; mt < BC / 32; ++mt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int kk = kb + 32 * mt + 8 * (e >> 2) + 4 * g + (e & 3);
+            const bool off = (kk >= kv_lim) | ((causal != 0) & (kk > q));
+            s[mt][e] = off ? -INFINITY : s[mt][e];
+          }
+      }
+#pragma unroll
+      for (int mt = 0; mt < BC / 32; ++mt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float p = fast_exp2(s[mt][e] * sl2 - lse2);
+          dp[mt][e] = p * (dp[mt][e] - Dq);
+        }
+      bf16x8 db[BC / 16], dl[PRECISE ? BC / 16 : 1];
+#pragma unroll
+      for (int c = 0; c < BC / 16; ++c) {
+        if constexpr (PRECISE)
+          pack_split_bf16x8(dp[c >> 1], 8 * (c & 1), db[c], dl[c]);
+        else
+          db[c] = pack_bf16x8(dp[c >> 1], 8 * (c & 1));
+      }
+      // dQ^T += K^T dS^T: A = K^T rows d = 32t + r, k-slots = keys of chunk c.
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+        for (int c = 0; c < BC / 16; ++c) {
+          const int r0 = 16 * c + tr_row, col = 32 * t + tr_col;
+          const bf16x8 aK = join_tr(ld_lds_tr(&Ks[buf][swz_off<D>(r0, col)]),
+                                    ld_lds_tr(&Ks[buf][swz_off<D>(r0 + 8, col)]));
+          acc[t] = mfma32(aK, db[c], acc[t]);
+          if constexpr (PRECISE) acc[t] = mfma32(aK, dl[c], acc[t]);
+        }
+    }
+    __syncthreads();
+  }
+
+  if (q < N) {
+    float* row = dQ + head + (size_t)q * D;
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f32x4 a;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) a[j] = acc[t][4 * i + j] * scale;
+        *reinterpret_cast<f32x4*>(row + 32 * t + 8 * i + 4 * g) = a;
+      }
+  }
+}
+
+template <int D, bool PRECISE, bool DQ_ATOMIC>
+static void launch_dkdv(const u16* q, const u16* k, const u16* v, const u16* g, const float* LSE,
+                        const float* Dws, float* dQ, float* dK, float* dV, const AttnShape& s, float sl2,
+                        hipStream_t stream) {
+  const int nkb = (s.N + DkdvCfg<D>::BKV - 1) / DkdvCfg<D>::BKV;
+  const int total = s.B * s.H * nkb;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, PRECISE, DQ_ATOMIC>), dim3(total), dim3(256), 0, stream, q, k, v, g,
+                     LSE, Dws, dQ, dK, dV, s.H, s.N, s.scale, sl2, s.causal, s.kv_len, nkb, total);
+}
+
+template <int D, bool PRECISE>
+static void launch_dq(const u16* q, const u16* k, const u16* v, const u16* g, const float* LSE,
+                      const float* Dws, float* dQ, const AttnShape& s, float sl2, hipStream_t stream) {
+  const int nqb = (s.N + DqCfg<D>::BR - 1) / DqCfg<D>::BR;
+  const int total = s.B * s.H * nqb;
+  hipLaunchKernelGGL((bwd_dq_kernel<D, PRECISE>), dim3(total), dim3(256), 0, stream, q, k, v, g, LSE,
+                     Dws, dQ, s.H, s.N, s.scale, sl2, s.causal, s.kv_len, nqb, total);
+}
+
+// Entry points of the per-head-size translation units.
+template <int D>
+static hipError_t launch_dkdv_any(const BwdArgs& a, const AttnShape& s, bool precise, bool dq_atomic,
+                                  hipStream_t stream) {
+  const float sl2 = s.scale * kLog2e;
+  const u16* q = static_cast<const u16*>(a.Q);
+  const u16* k = static_cast<const u16*>(a.K);
+  const u16* v = static_cast<const u16*>(a.V);
+  const u16* g = static_cast<const u16*>(a.dO);
+  if (dq_atomic) {
+    if (precise)
+      launch_dkdv<D, true, true>(q, k, v, g, a.LSE, a.Dws, a.dQ, a.dK, a.dV, s, sl2, stream);
+    else
+      launch_dkdv<D, false, true>(q, k, v, g, a.LSE, a.Dws, a.dQ, a.dK, a.dV, s, sl2, stream);
+  } else if (precise) {
+    launch_dkdv<D, true, false>(q, k, v, g, a.LSE, a.Dws, a.dQ, a.dK, a.dV, s, sl2, stream);
+  } else {
+    launch_dkdv<D, false, false>(q, k, v, g, a.LSE, a.Dws, a.dQ, a.dK, a.dV, s, sl2, stream);
+  }
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_dq_any(const BwdArgs& a, const AttnShape& s, bool precise, hipStream_t stream) {
+  const float sl2 = s.scale * kLog2e;
+  const u16* q = static_cast<const u16*>(a.Q);
+  const u16* k = static_cast<const u16*>(a.K);
+  const u16* v = static_cast<const u16*>(a.V);
+  const u16* g = static_cast<const u16*>(a.dO);
+  if (precise)
+    launch_dq<D, true>(q, k, v, g, a.LSE, a.Dws, a.dQ, s, sl2, stream);
+  else
+    launch_dq<D, false>(q, k, v, g, a.LSE, a.Dws, a.dQ, s, sl2, stream);
+  return hipGetLastError();
+}
+
+}  // namespace fa

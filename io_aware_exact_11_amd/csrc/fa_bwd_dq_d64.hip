@@ -1,0 +1,10 @@
+// Query-outer backward kernel (dQ) instantiated for head size 64.
+#include "fa_bwd.h"
+
+namespace fa {
+
+hipError_t launch_dq_bf16_d64(const BwdArgs& a, const AttnShape& s, bool precise, hipStream_t stream) {
+  return launch_dq_any<64>(a, s, precise, stream);
+}
+
+}  // namespace fa

@@ -1,282 +1,12 @@
-// Forward pass of exact attention for gfx950, bf16 in, fp32 accumulation.
-//
-// One workgroup owns BR = 128 query rows of one (b, h) and streams the keys
-// and values through LDS in tiles of BC = 64 rows, double-buffered: the
-// global loads of tile j+1 are in flight while tile j is computed
-// ("FlashAttention and GPU Memory", chapter 07 Blocks: one block of Q stays
-// on chip while blocks of K and V come in; only O and the row statistics
-// are written back).
-//
-// Each of the 4 waves owns 32 query rows. Scores are produced transposed,
-// S^T = K Q^T, with the 32x32x16 bf16 matrix-core product: A = a K tile
-// from LDS, B = the wave's Q fragment held in registers for the whole loop.
-// In that layout each lane holds one query's scores for 32 of the tile's
-// keys and its partner lane (lane ^ 32) the other 32, so the running
-// maximum needs one cross-lane exchange per tile and the running sum none
-// (each lane keeps a partial sum; the halves are added once at the end).
-//
-// Running softmax ("FlashAttention and GPU Memory", chapter 08): m is kept
-// in base-2 units of the scaled score, m' = max(m, max_j s_j * scale*log2e),
-// P~ = 2^(s*scale*log2e - m'), l' = 2^(m-m') l + sum P~, and the unnormalised
-// output is rescaled by the same 2^(m-m'). O is divided by l once, after
-// the last tile, and LSE = (m + log2 l) ln 2 is stored for the backward.
-//
-// The P~ V product reuses the score registers directly as its B operand
-// (O^T = V^T P^T): the 8 k-slots a lane feeds are 8 of its own score
-// elements. Its A operand is V transposed; V tiles stay row-major in LDS and
-// are read transposed with ds_read_b64_tr_b16, two reads per operand, with
-// the key order chosen to match those slots.
-//
-// The running maximum moves lazily: only when a tile's maximum exceeds it by
-// more than 8 (base 2), which keeps every weight below 2^8 and skips the O
-// rescale on almost every tile. Loads go through buffer resources, whose
-// hardware bounds check returns zeros past the end of a head.
-#include "fa_common.h"
+// Forward dispatch by head size.
 #include "fa_launch.h"
 
 namespace fa {
 
-template <int D>
-struct FwdCfg {
-  static constexpr int NW = 4;                  // waves per workgroup
-  static constexpr int BR = 32 * NW;            // query rows per workgroup
-  static constexpr int BC = 64;                 // keys per tile
-  static constexpr int KSTR = D + 8;            // K tile row stride (elements)
-  static constexpr int VSTR = D + 32;           // V tile row stride: the 4 rows of a transposing read land 16 banks apart
-  static constexpr int CH = BC * D / 8 / 256;   // 16-byte chunks per thread per tile
-  static_assert(D == 64 || D == 128, "head dim");
-};
-
-// Rescale threshold, in base-2 units of the scaled score: the running
-// maximum only moves (and O, l are only rescaled) when a tile's maximum
-// exceeds it by more than this, so unnormalised weights stay below 2^8.
-constexpr float kRescaleSlack = 8.f;
-
-template <int D>
-__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
-    const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
-    u16* __restrict__ O, float* __restrict__ LSE, int H, int N, float sl2, int causal,
-    const int32_t* __restrict__ kv_len, int nqb, int total) {
-  using C = FwdCfg<D>;
-  constexpr int BC = C::BC;
-  __shared__ __attribute__((aligned(16))) u16 Ks[2][BC * C::KSTR];
-  __shared__ __attribute__((aligned(16))) u16 Vs[2][BC * C::VSTR];
-
-  const int tile = xcd_tile(blockIdx.x, total);
-  int qb = tile % nqb;
-  const int bh = tile / nqb;
-  if (causal) qb = nqb - 1 - qb;  // longest rows first
-  const int b = bh / H;
-  const int q0 = qb * C::BR;
-  const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, r = lane & 31, g = lane >> 5;
-  const size_t head = (size_t)bh * N * D;
-  const unsigned head_bytes = (unsigned)N * D * 2;
-  const auto rQ = make_rsrc(Q + head, head_bytes);
-  const auto rK = make_rsrc(K + head, head_bytes);
-  const auto rV = make_rsrc(V + head, head_bytes);
-
-  int kv_lim = N;
-  if (kv_len) {
-    const int L = kv_len[b];
-    kv_lim = L < 0 ? 0 : (L > N ? N : L);
-  }
-  int kv_end = kv_lim;
-  if (causal) kv_end = min(kv_end, q0 + C::BR);
-  const int nt = (kv_end + BC - 1) / BC;
-
-  const int q = q0 + 32 * w + r;  // this lane's query row
-  const int wave_q_first = q0 + 32 * w;
-  const int wave_q_last = wave_q_first + 31;
-
-  // Q fragment: B operand of S^T = K Q^T (column = query, k = d).
-  bf16x8 qf[D / 16];
-#pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk)
-    qf[kk] = as_bf16x8(ld_buf16(rQ, (unsigned)(q * D + 16 * kk + 8 * g) * 2));
-
-  f32x16 o[D / 32];
-#pragma unroll
-  for (int t = 0; t < D / 32; ++t)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) o[t][e] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
-
-  // Tile loads: chunk c = tid + 256*rr is row c / (D/8), 16-byte column c % (D/8).
-  u32x4 kreg[C::CH], vreg[C::CH];
-  auto tile_off = [&](int kb, int rr) {
-    const int c = tid + 256 * rr;
-    return (unsigned)((kb + c / (D / 8)) * D + (c % (D / 8)) * 8) * 2;
-  };
-  auto load_k = [&](int kb) {
-#pragma unroll
-    for (int rr = 0; rr < C::CH; ++rr) kreg[rr] = ld_buf16(rK, tile_off(kb, rr));
-  };
-  auto load_v = [&](int kb) {
-#pragma unroll
-    for (int rr = 0; rr < C::CH; ++rr) vreg[rr] = ld_buf16(rV, tile_off(kb, rr));
-  };
-  auto store_k = [&](int buf) {
-#pragma unroll
-    for (int rr = 0; rr < C::CH; ++rr) {
-      const int c = tid + 256 * rr;
-      *reinterpret_cast<u32x4*>(&Ks[buf][(c / (D / 8)) * C::KSTR + (c % (D / 8)) * 8]) = kreg[rr];
-    }
-  };
-  auto store_v = [&](int buf) {
-#pragma unroll
-    for (int rr = 0; rr < C::CH; ++rr) {
-      const int c = tid + 256 * rr;
-      *reinterpret_cast<u32x4*>(&Vs[buf][(c / (D / 8)) * C::VSTR + (c % (D / 8)) * 8]) = vreg[rr];
-    }
-  };
-  // S^T tile from K buffer `buf`: rows = keys 32*mt + (8i + 4g + j), column = query q.
-  auto qk = [&](int buf, f32x16* s) {
-#pragma unroll
-    for (int mt = 0; mt < BC / 32; ++mt) {
-      const u16* kp = &Ks[buf][(32 * mt + r) * C::KSTR + 8 * g];
-      s[mt] = mfma32_first(ld_lds16(kp), qf[0]);
-#pragma unroll
-      for (int kk = 1; kk < D / 16; ++kk) s[mt] = mfma32(ld_lds16(kp + 16 * kk), qf[kk], s[mt]);
-    }
-  };
-  // Per-lane offsets of the transposing V reads (see ld_lds_tr): row part
-  // 4g + (lane % 16) / 4, column part 16 * ((lane / 16) % 2) + 4 * (lane % 4).
-  const int v_tr_off = (4 * g + ((lane & 15) >> 2)) * C::VSTR + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  // Causal waves compute only the tiles that reach their rows (a prefix).
-  const int nt_w = causal ? min(nt, wave_q_last / BC + 1) : nt;
-
-  // Software pipeline: K runs one tile ahead of V, so while tile j's softmax
-  // is on the vector ALUs the wave already issues tile j+1's S^T products.
-  // Buffers: K_j in Ks[j % 2], V_j in Vs[j % 2]; one barrier per tile.
-  if (nt > 0) {
-    load_k(0);
-    load_v(0);
-    store_k(0);
-    store_v(0);
-  }
-  if (nt > 1) {
-    load_k(BC);
-    store_k(1);
-  }
-  __syncthreads();
-  f32x16 s_cur[BC / 32];
-  if (nt_w > 0) qk(0, s_cur);
-  // K_0's buffer is refilled with K_2 during the first tile: every wave must
-  // have taken its scores from it first.
-  __syncthreads();
-
-  for (int it = 0; it < nt; ++it) {
-    const int kb = it * BC;
-    const bool more_k = it + 2 < nt, more_v = it + 1 < nt;
-    if (more_k) load_k(kb + 2 * BC);
-    if (more_v) load_v(kb + BC);
-
-    if (it < nt_w) {
-      const bool need_mask = (kb + BC > kv_lim) || (causal && kb + BC - 1 > wave_q_first);
-      if (need_mask) {
-#pragma unroll
-        for (int mt = 0; mt < BC / 32; ++mt)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int key = kb + 32 * mt + 8 * (e >> 2) + 4 * g + (e & 3);
-            const bool off = (key >= kv_lim) | ((causal != 0) & (key > q));
-            s_cur[mt][e] = off ? -INFINITY : s_cur[mt][e];
-          }
-      }
-
-      float mx = s_cur[0][0];
-#pragma unroll
-      for (int mt = 0; mt < BC / 32; ++mt)
-#pragma unroll
-        for (int e = (mt == 0 ? 1 : 0); e < 16; ++e) mx = fmaxf(mx, s_cur[mt][e]);
-      const float tmax = pair_max(mx) * sl2;
-      // Move the reference maximum only when some row of the wave outgrows it.
-      if (__builtin_amdgcn_ballot_w64(tmax > m_run + kRescaleSlack) != 0) {
-        const float m_new = fmaxf(m_run, tmax);
-        const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int t = 0; t < D / 32; ++t)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) o[t][e] *= alpha;
-        m_run = m_new;
-      }
-      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-
-      // Next tile's scores (on the last tile this reads a stale buffer and
-      // the result is dropped), independent of the softmax below.
-      f32x16 s_next[BC / 32];
-      qk((it + 1) & 1, s_next);
-
-      float rs = 0.f;
-#pragma unroll
-      for (int mt = 0; mt < BC / 32; ++mt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float p = fast_exp2(s_cur[mt][e] * sl2 - m_use);
-          s_cur[mt][e] = p;
-          rs += p;
-        }
-      l_run += rs;
-
-      bf16x8 pb[BC / 16];
-#pragma unroll
-      for (int c = 0; c < BC / 16; ++c) pb[c] = pack_bf16x8(s_cur[c >> 1], 8 * (c & 1));
-      // O^T += V^T P^T: A = V^T rows d = 32t + r, k-slots = keys of chunk c in
-      // the order of the score registers (16c + 8h + 4g + 0..3 for slots 4h..4h+3).
-      const u16* vb = &Vs[it & 1][v_tr_off];
-#pragma unroll
-      for (int t = 0; t < D / 32; ++t)
-#pragma unroll
-        for (int c = 0; c < BC / 16; ++c) {
-          const u16* vp = vb + (16 * c) * C::VSTR + 32 * t;
-          o[t] = mfma32(join_tr(ld_lds_tr(vp), ld_lds_tr(vp + 8 * C::VSTR)), pb[c], o[t]);
-        }
-#pragma unroll
-      for (int mt = 0; mt < BC / 32; ++mt) s_cur[mt] = s_next[mt];
-    }
-
-    if (more_k) store_k(it & 1);
-    if (more_v) store_v((it + 1) & 1);
-    __syncthreads();
-  }
-
-  const float l_tot = pair_sum(l_run);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (q < N) {
-    u16* orow = O + head + (size_t)q * D;
-#pragma unroll
-    for (int t = 0; t < D / 32; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        u32x2 p;
-        __bf16 h0 = (__bf16)(o[t][4 * i + 0] * inv), h1 = (__bf16)(o[t][4 * i + 1] * inv);
-        __bf16 h2 = (__bf16)(o[t][4 * i + 2] * inv), h3 = (__bf16)(o[t][4 * i + 3] * inv);
-        p[0] = (unsigned)__builtin_bit_cast(u16, h0) | ((unsigned)__builtin_bit_cast(u16, h1) << 16);
-        p[1] = (unsigned)__builtin_bit_cast(u16, h2) | ((unsigned)__builtin_bit_cast(u16, h3) << 16);
-        *reinterpret_cast<u32x2*>(orow + 32 * t + 8 * i + 4 * g) = p;
-      }
-    if (g == 0) LSE[(size_t)bh * N + q] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
-  }
-}
-
-template <int D>
-static hipError_t launch_fwd_d(const void* Q, const void* K, const void* V, void* O, float* LSE,
-                               const AttnShape& s, hipStream_t stream) {
-  const int nqb = (s.N + FwdCfg<D>::BR - 1) / FwdCfg<D>::BR;
-  const int total = s.B * s.H * nqb;
-  hipLaunchKernelGGL(fwd_bf16_kernel<D>, dim3(total), dim3(256), 0, stream,
-                     static_cast<const u16*>(Q), static_cast<const u16*>(K),
-                     static_cast<const u16*>(V), static_cast<u16*>(O), LSE, s.H, s.N,
-                     s.scale * kLog2e, s.causal, s.kv_len, nqb, total);
-  return hipGetLastError();
-}
-
 hipError_t launch_fwd_bf16(const void* Q, const void* K, const void* V, void* O, float* LSE,
                            const AttnShape& s, hipStream_t stream) {
-  if (s.d == 64) return launch_fwd_d<64>(Q, K, V, O, LSE, s, stream);
-  return launch_fwd_d<128>(Q, K, V, O, LSE, s, stream);
+  if (s.d == 64) return launch_fwd_bf16_d64(Q, K, V, O, LSE, s, stream);
+  return launch_fwd_bf16_d128(Q, K, V, O, LSE, s, stream);
 }
 
 }  // namespace fa

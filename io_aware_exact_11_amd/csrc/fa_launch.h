@@ -16,8 +16,29 @@ struct AttnShape {
   const int32_t* kv_len;  // device [B] or nullptr
 };
 
+// Device pointers of one backward call. Q, K, V, O, dO are bf16 (or fp32
+// for the fp32 path); Dws is the fp32 [B,H,N] scratch for D_i.
+struct BwdArgs {
+  const void *Q, *K, *V, *O, *dO;
+  const float* LSE;
+  float *dQ, *dK, *dV, *Dws;
+};
+
 hipError_t launch_fwd_bf16(const void* Q, const void* K, const void* V, void* O, float* LSE,
                            const AttnShape& s, hipStream_t stream);
+
+// Per-head-size pieces, each in a translation unit of its own so that each
+// can be compiled with the instruction-scheduling options that suit it.
+hipError_t launch_fwd_bf16_d64(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                               const AttnShape& s, hipStream_t stream);
+hipError_t launch_fwd_bf16_d128(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                                const AttnShape& s, hipStream_t stream);
+hipError_t launch_dkdv_bf16_d64(const BwdArgs& a, const AttnShape& s, bool precise, bool dq_atomic,
+                                hipStream_t stream);
+hipError_t launch_dkdv_bf16_d128(const BwdArgs& a, const AttnShape& s, bool precise, bool dq_atomic,
+                                 hipStream_t stream);
+hipError_t launch_dq_bf16_d64(const BwdArgs& a, const AttnShape& s, bool precise, hipStream_t stream);
+hipError_t launch_dq_bf16_d128(const BwdArgs& a, const AttnShape& s, bool precise, hipStream_t stream);
 
 // Dws: fp32 [B,H,N] scratch for the per-row term D_i.
 hipError_t launch_bwd_bf16(const void* Q, const void* K, const void* V, const void* O,
