@@ -330,6 +330,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     load(qb_start * BQ);
     store(0);
     __syncthreads();
+    wait_vmem_all();
     for (int qb = qb_start; qb < nqb; ++qb) {
       const int q0 = qb * BQ;
       const int buf = (qb - qb_start) & 1;

@@ -82,6 +82,13 @@ __device__ __forceinline__ bf16x8 ld_lds16(const u16* p) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// s_waitcnt vmcnt(0): wait for every outstanding vector-memory load of the
+// wave. Used at the end of a prologue whose loads complete on some control
+// paths only: the compiler's wait bookkeeping merges paths, so a load left
+// pending on one path would otherwise be waited for inside the main loop,
+// behind the loop's own prefetches. (Encoding: vmcnt 0, expcnt 7, lgkmcnt 15.)
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Round 8 fp32 values to bf16 (round to nearest even) as one MFMA operand.
 __device__ __forceinline__ bf16x8 pack_bf16x8(const f32x16& v, int base) {
   bf16x8 r;

@@ -272,6 +272,7 @@ __global__ __launch_bounds__(C::NT, C::OCC * 4 / C::NW) void fwd_bf16_kernel(
     // K_0's buffer is refilled with K_2 during the first tile: every wave
     // must have taken its scores from it first.
     __syncthreads();
+    wait_vmem_all();
 
     for (int it = 0; it < nt; ++it) {
       const int kb = it * BC;
@@ -304,6 +305,7 @@ __global__ __launch_bounds__(C::NT, C::OCC * 4 / C::NW) void fwd_bf16_kernel(
       store_v(0);
     }
     __syncthreads();
+    wait_vmem_all();
     for (int it = 0; it < nt; ++it) {
       const int kb = it * BC;
       const bool more = it + 1 < nt;
