@@ -24,6 +24,8 @@
 // waves whose keys are all invisible to a block skip its products.
 #pragma once
 
+#include <climits>
+
 #include "fa_common.h"
 #include "fa_launch.h"
 
@@ -174,13 +176,15 @@ __global__ __launch_bounds__(256, 2) void bwd_exact_d_kernel(
         }
       }
       const bool need_mask = (kb + BC > kv_lim) || (causal && kb + BC - 1 > wave_q_first);
+      // Key kb + 4g + c, c = 32mt + 8(e/4) + e%4, is hidden iff c > lim.
+      const int lim = need_mask ? min(kv_lim - 1, causal ? q : kv_lim - 1) - (kb + 4 * g) : INT_MAX;
 #pragma unroll
       for (int mt = 0; mt < BC / 32; ++mt)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int key = kb + 32 * mt + 8 * (e >> 2) + 4 * g + (e & 3);
+          const int c = 32 * mt + 8 * (e >> 2) + (e & 3);
           float p = fast_exp2(s[mt][e] * sl2 - lse2);
-          if (need_mask && (key >= kv_lim || (causal && key > q))) p = 0.f;
+          if (c > lim) p = 0.f;
           part += p * dp[mt][e];
         }
     }
@@ -352,13 +356,16 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
         }
         // Masked scores become -inf, so their weights come out exactly 0.
         if ((kw0 + 31 >= kv_lim) || (causal && q0 < kw0 + 31)) {
+          // Element e of tile qt is query q0 + 4g + c with the constant
+          // c = 32qt + 8(e/4) + e%4; this lane's key is hidden from it iff the
+          // key is >= kv_lim (every c) or, causal, key > query (c < lim).
+          const int lim = key >= kv_lim ? INT_MAX : (causal ? key - q0 - 4 * g : INT_MIN);
 #pragma unroll
           for (int qt = 0; qt < BQ / 32; ++qt)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-              const int qq = q0 + 32 * qt + 8 * (e >> 2) + 4 * g + (e & 3);
-              const bool off = (key >= kv_lim) | ((causal != 0) & (key > qq));
-              sa[qt][e] = off ? -INFINITY : sa[qt][e];
+              const int c = 32 * qt + 8 * (e >> 2) + (e & 3);
+              sa[qt][e] = c < lim ? -INFINITY : sa[qt][e];
             }
         }
 #pragma unroll
@@ -577,13 +584,14 @@ __global__ __launch_bounds__(256, PRECISE ? 1 : 2) void bwd_dq_kernel(
         }
       }
       if ((kb + BC > kv_lim) || (causal && kb + BC - 1 > wave_q_first)) {
+        // Key kb + 4g + c, c = 32mt + 8(e/4) + e%4, is hidden iff c > lim.
+        const int lim = min(kv_lim - 1, causal ? q : kv_lim - 1) - (kb + 4 * g);
 #pragma unroll
         for (int mt = 0; mt < BC / 32; ++mt)
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
-            const int kk = kb + 32 * mt + 8 * (e >> 2) + 4 * g + (e & 3);
-            const bool off = (kk >= kv_lim) | ((causal != 0) & (kk > q));
-            s[mt][e] = off ? -INFINITY : s[mt][e];
+            const int c = 32 * mt + 8 * (e >> 2) + (e & 3);
+            s[mt][e] = c > lim ? -INFINITY : s[mt][e];
           }
       }
 #pragma unroll

@@ -190,13 +190,16 @@ __global__ __launch_bounds__(C::NT, C::OCC * 4 / C::NW) void fwd_bf16_kernel(
       const int q = slab_first + r;
       const bool need_mask = (kb + BC > kv_lim) || (causal && kb + BC - 1 > slab_first);
       if (need_mask) {
+        // Element e of score tile mt is key kb + 4g + c with the constant
+        // c = 32mt + 8(e/4) + e%4; the key is hidden iff it is >= kv_lim or
+        // (causal) > q, i.e. iff c > lim: one compare and select per score.
+        const int lim = min(kv_lim - 1, causal ? q : kv_lim - 1) - (kb + 4 * g);
 #pragma unroll
         for (int mt = 0; mt < BC / 32; ++mt)
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
-            const int key = kb + 32 * mt + 8 * (e >> 2) + 4 * g + (e & 3);
-            const bool off = (key >= kv_lim) | ((causal != 0) & (key > q));
-            sv[s][mt][e] = off ? -INFINITY : sv[s][mt][e];
+            const int c = 32 * mt + 8 * (e >> 2) + (e & 3);
+            sv[s][mt][e] = c > lim ? -INFINITY : sv[s][mt][e];
           }
       }
       float mx = sv[s][0][0];
