@@ -209,9 +209,7 @@ template <int D>
 struct DkdvCfg {
   static constexpr int NW = 4;
   static constexpr int BKV = 32 * NW;          // keys per workgroup (32 per wave)
-  // query rows per block: 64 at d=128; 32 at d=64, where the smaller blocks
-  // measured faster (shorter sequences, lighter per-block products)
-  static constexpr int BQ = D == 128 ? 64 : 32;
+  static constexpr int BQ = 64;                // query rows per block
   static constexpr int CH = BQ * D / 8 / 256;  // 16-byte chunks per thread per tensor
   static constexpr int KCH = BKV * D / 8 / 256;
   static constexpr int DSTR = BKV + 8;         // dS tile row stride (row reads only)
@@ -503,11 +501,16 @@ struct DqCfg {
 // (swizzled) K tile through transposing reads. K and V tiles arrive by
 // direct buffer-to-LDS loads, double-buffered, which keeps the kernel's
 // registers within two waves per SIMD without spilling.
+//
+// Outside precise mode the kernel also forms the per-row term itself,
+// D_i = dO_i . O_i, from the dO rows it already holds and one read of O, and
+// stores it to Dg for the dK/dV kernel that runs after it (no separate
+// pre-pass). In precise mode it reads the exact D_i from Dg.
 template <int D, bool PRECISE>
 __global__ __launch_bounds__(256, PRECISE ? 1 : 2) void bwd_dq_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
-    const u16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dg,
-    float* __restrict__ dQ, int H, int N, float scale, float sl2, int causal,
+    const u16* __restrict__ O, const u16* __restrict__ dO, const float* __restrict__ LSE,
+    float* __restrict__ Dg, float* __restrict__ dQ, int H, int N, float scale, float sl2, int causal,
     const int32_t* __restrict__ kv_len, int nqb, int total) {
   using C = DqCfg<D>;
   constexpr int BC = C::BC;
@@ -549,7 +552,25 @@ __global__ __launch_bounds__(256, PRECISE ? 1 : 2) void bwd_dq_kernel(
     df[kk] = as_bf16x8(ld_buf16(rO, off));
   }
   const float lse2 = q < N ? LSE[(size_t)bh * N + q] * kLog2e : INFINITY;
-  const float Dq = q < N ? Dg[(size_t)bh * N + q] : 0.f;
+  float Dq;
+  if constexpr (PRECISE) {
+    Dq = q < N ? Dg[(size_t)bh * N + q] : 0.f;
+  } else {
+    // This lane holds d-chunks 16kk + 8g .. +7 of the row's dO; its partner
+    // lane (lane ^ 32) holds the other half. Rows past N read zeros.
+    const auto rOut = make_rsrc(O + head, head_bytes);
+    float part = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const u32x4 ov = ld_buf16(rOut, (unsigned)(q * D + 16 * kk + 8 * g) * 2);
+      const u32x4 gv = __builtin_bit_cast(u32x4, df[kk]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        part += __uint_as_float(bf16_bits(ov, e) << 16) * __uint_as_float(bf16_bits(gv, e) << 16);
+    }
+    Dq = pair_sum(part);
+    if (q < N && g == 0) Dg[(size_t)bh * N + q] = Dq;
+  }
 
   f32x16 acc[D / 32];
 #pragma unroll
@@ -649,11 +670,12 @@ static void launch_dkdv(const u16* q, const u16* k, const u16* v, const u16* g, 
 }
 
 template <int D, bool PRECISE>
-static void launch_dq(const u16* q, const u16* k, const u16* v, const u16* g, const float* LSE,
-                      const float* Dws, float* dQ, const AttnShape& s, float sl2, hipStream_t stream) {
+static void launch_dq(const u16* q, const u16* k, const u16* v, const u16* o, const u16* g,
+                      const float* LSE, float* Dws, float* dQ, const AttnShape& s, float sl2,
+                      hipStream_t stream) {
   const int nqb = (s.N + DqCfg<D>::BR - 1) / DqCfg<D>::BR;
   const int total = s.B * s.H * nqb;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, PRECISE>), dim3(total), dim3(256), 0, stream, q, k, v, g, LSE,
+  hipLaunchKernelGGL((bwd_dq_kernel<D, PRECISE>), dim3(total), dim3(256), 0, stream, q, k, v, o, g, LSE,
                      Dws, dQ, s.H, s.N, s.scale, sl2, s.causal, s.kv_len, nqb, total);
 }
 
@@ -685,11 +707,12 @@ static hipError_t launch_dq_any(const BwdArgs& a, const AttnShape& s, bool preci
   const u16* q = static_cast<const u16*>(a.Q);
   const u16* k = static_cast<const u16*>(a.K);
   const u16* v = static_cast<const u16*>(a.V);
+  const u16* o = static_cast<const u16*>(a.O);
   const u16* g = static_cast<const u16*>(a.dO);
   if (precise)
-    launch_dq<D, true>(q, k, v, g, a.LSE, a.Dws, a.dQ, s, sl2, stream);
+    launch_dq<D, true>(q, k, v, o, g, a.LSE, a.Dws, a.dQ, s, sl2, stream);
   else
-    launch_dq<D, false>(q, k, v, g, a.LSE, a.Dws, a.dQ, s, sl2, stream);
+    launch_dq<D, false>(q, k, v, o, g, a.LSE, a.Dws, a.dQ, s, sl2, stream);
   return hipGetLastError();
 }
 

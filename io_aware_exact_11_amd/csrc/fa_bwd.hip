@@ -1,6 +1,8 @@
-// Backward orchestration: the per-row term D_i (pre-pass), then the
-// key-outer dK/dV kernel and the query-outer dQ kernel of the matching head
-// size (or the key-outer kernel alone, accumulating dQ with atomics).
+// Backward orchestration. Default: the query-outer dQ kernel (which also
+// forms the per-row term D_i = dO_i . O_i), then the key-outer dK/dV kernel.
+// Precise mode: an exact-D pre-pass, then both kernels. Atomic-dQ mode: the
+// rowsum(dO o O) pre-pass, then the key-outer kernel alone, accumulating dQ
+// with atomics.
 #include "fa_bwd.h"
 
 namespace fa {
@@ -51,6 +53,14 @@ hipError_t launch_bwd_bf16(const void* Q, const void* K, const void* V, const vo
   if (dq_atomic) {
     e = fill_zero(dQ, (size_t)s.B * s.H * s.N * s.d, stream);
     if (e != hipSuccess) return e;
+  }
+  if (!precise && !dq_atomic) {
+    // The dQ kernel forms D_i = dO_i . O_i itself and stores it for the
+    // dK/dV kernel, which therefore runs second.
+    e = d64 ? launch_dq_bf16_d64(a, s, false, stream) : launch_dq_bf16_d128(a, s, false, stream);
+    if (e != hipSuccess) return e;
+    return d64 ? launch_dkdv_bf16_d64(a, s, false, false, stream)
+               : launch_dkdv_bf16_d128(a, s, false, false, stream);
   }
   e = d64 ? launch_row_term<64>(a, s, precise, stream) : launch_row_term<128>(a, s, precise, stream);
   if (e != hipSuccess) return e;
