@@ -53,7 +53,11 @@ struct FwdCfg {
   static constexpr int BR = 32 * NW * QS;       // query rows per workgroup
   static constexpr int BC = 64;                 // keys per tile
   static constexpr int KSTR = D + 8;            // K tile row stride (elements)
-  static constexpr int VSTR = D + 32;           // V tile row stride: the 4 rows of a transposing read land 16 banks apart
+  // V tile row stride: the 4 rows of a transposing read must land in
+  // disjoint banks (16 banks apart at d=128; at d=64 a stride of D+8 already
+  // places them 36 banks apart, and the smaller tile lets four workgroups
+  // share a CU).
+  static constexpr int VSTR = D == 64 ? D + 8 : D + 32;
   static constexpr int CH = BC * D / 8 / NT;    // 16-byte chunks per thread per tile
   static_assert(D == 64 || D == 128, "head dim");
   static_assert(CH * NT * 8 == BC * D, "tile split");
@@ -61,11 +65,13 @@ struct FwdCfg {
 
 // Measured choices. d=128: one slab per wave, pipelined, two waves per SIMD
 // (two slabs need more than the 256 registers of two waves per SIMD, and one
-// wave per SIMD measured slower). d=64: the same for causal attention; for
-// non-causal attention two slabs per wave, unpipelined, still at two waves
-// per SIMD, which halves the LDS operand reads per product.
+// wave per SIMD measured slower). d=64 causal: one slab, unpipelined, four
+// waves per SIMD: causal workgroups are short, and more of them in flight
+// hide their start-up latency better than the pipeline does. d=64
+// non-causal: two slabs per wave, unpipelined, two waves per SIMD, which
+// halves the LDS operand reads per product.
 using FwdCfg128 = FwdCfg<128, 4, 1, true, 2>;
-using FwdCfg64Causal = FwdCfg<64, 4, 1, true, 2>;
+using FwdCfg64Causal = FwdCfg<64, 4, 1, false, 4>;
 using FwdCfg64Full = FwdCfg<64, 4, 2, false, 2>;
 
 // Rescale threshold, in base-2 units of the scaled score: the running
