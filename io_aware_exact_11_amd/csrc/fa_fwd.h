@@ -1,13 +1,13 @@
 // Forward pass of exact attention for gfx950, bf16 in, fp32 accumulation.
 //
-// One workgroup owns BR = 128 query rows of one (b, h) and streams the keys
-// and values through LDS in tiles of BC = 64 rows, double-buffered: the
-// global loads of tile j+1 are in flight while tile j is computed
-// ("FlashAttention and GPU Memory", chapter 07 Blocks: one block of Q stays
-// on chip while blocks of K and V come in; only O and the row statistics
-// are written back).
+// One workgroup owns BR query rows of one (b, h) (128, or 256 with two slabs
+// per wave) and streams the keys and values through LDS in tiles of BC = 64
+// rows, double-buffered: the global loads of the next tile are in flight
+// while the current one is computed ("FlashAttention and GPU Memory",
+// chapter 07 Blocks: one block of Q stays on chip while blocks of K and V
+// come in; only O and the row statistics are written back).
 //
-// Each of the 4 waves owns 32 query rows. Scores are produced transposed,
+// Each of the 4 waves owns one or two 32-row query slabs. Scores are produced transposed,
 // S^T = K Q^T, with the 32x32x16 bf16 matrix-core product: A = a K tile
 // from LDS, B = the wave's Q fragment held in registers for the whole loop.
 // In that layout each lane holds one query's scores for 32 of the tile's
