@@ -162,6 +162,33 @@ __device__ __forceinline__ void tile_to_lds(__amdgpu_buffer_rsrc_t rs, int row0,
   }
 }
 
+// Direct-to-LDS copy of ROWS rows of D bf16 into a tile whose rows are
+// STRIDE elements apart (padding keeps the row-wise and transposing reads
+// free of bank conflicts). Each wave instruction fills 1 KB of LDS, 16
+// bytes per lane at consecutive addresses; lane l of block blk covers tile
+// byte 1024*blk + 16*l, i.e. row (that offset) / (2*STRIDE) and byte
+// (that offset) % (2*STRIDE) of the row, which it fetches from the global
+// row. Lanes that land in a row's padding re-read the row's first chunk.
+// Rows past the end of the buffer resource read zeros.
+template <int D, int STRIDE, int ROWS, int NW>
+__device__ __forceinline__ void tile_to_lds_padded(__amdgpu_buffer_rsrc_t rs, int row0, u16* tile, int w,
+                                                   int lane) {
+  constexpr int BYTES = ROWS * STRIDE * 2;
+  static_assert(BYTES % 1024 == 0, "whole 1 KB blocks");
+  constexpr int NBLK = BYTES / 1024;
+#pragma unroll
+  for (int i = 0; i < (NBLK + NW - 1) / NW; ++i) {
+    const int blk = w + NW * i;
+    if (NBLK % NW == 0 || blk < NBLK) {
+      const int off = blk * 1024 + lane * 16;
+      const int row = off / (STRIDE * 2), cb = off % (STRIDE * 2);
+      const int src = (row0 + row) * D * 2 + (cb < D * 2 ? cb : 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)(tile + blk * 512), 16, src, 0, 0, 0);
+    }
+  }
+}
+
 // Map a linear workgroup id to a tile id so that the tiles of one (b, h)
 // run on one XCD, in order: workgroups are dispatched round-robin over the
 // 8 XCDs, each with its own L2, and neighbouring tiles of a head share K, V.

@@ -33,6 +33,8 @@
 // hardware bounds check returns zeros past the end of a head.
 #pragma once
 
+#include <type_traits>
+
 #include "fa_common.h"
 #include "fa_launch.h"
 
@@ -42,13 +44,17 @@ namespace fa {
 // query rows; every K and V operand read from LDS feeds QS matrix-core
 // products, so LDS read traffic per flop falls as 1/QS. PIPE runs the
 // score products of tile j+1 ahead of the softmax of tile j; OCC is the
-// number of waves per SIMD the register budget is cut for.
-template <int D, int NW_, int QS_, bool PIPE_, int OCC_>
+// number of waves per SIMD the register budget is cut for. DL (with PIPE)
+// moves K and V tiles from global memory straight into LDS with buffer
+// loads that bypass the registers, instead of staging them in registers.
+template <int D, int NW_, int QS_, bool PIPE_, int OCC_, bool DL_ = false>
 struct FwdCfg {
   static constexpr int NW = NW_;
   static constexpr int QS = QS_;
   static constexpr bool PIPE = PIPE_;
   static constexpr int OCC = OCC_;
+  static constexpr bool DL = DL_;
+  static_assert(!DL || PIPE, "direct loads are implemented for the pipelined loop");
   static constexpr int NT = 64 * NW;            // threads per workgroup
   static constexpr int BR = 32 * NW * QS;       // query rows per workgroup
   static constexpr int BC = 64;                 // keys per tile
@@ -63,14 +69,15 @@ struct FwdCfg {
   static_assert(CH * NT * 8 == BC * D, "tile split");
 };
 
-// Measured choices. d=128: one slab per wave, pipelined, two waves per SIMD
-// (two slabs need more than the 256 registers of two waves per SIMD, and one
-// wave per SIMD measured slower). d=64 causal: one slab, unpipelined, four
+// Measured choices. d=128: one slab per wave, pipelined, direct-to-LDS
+// tile loads, two waves per SIMD (two slabs need more than the 256
+// registers of two waves per SIMD, and one wave per SIMD measured slower;
+// register-staged loads measured 9% slower). d=64 causal: one slab, unpipelined, four
 // waves per SIMD: causal workgroups are short, and more of them in flight
 // hide their start-up latency better than the pipeline does. d=64
 // non-causal: two slabs per wave, unpipelined, two waves per SIMD, which
 // halves the LDS operand reads per product.
-using FwdCfg128 = FwdCfg<128, 4, 1, true, 2>;
+using FwdCfg128 = FwdCfg<128, 4, 1, true, 2, true>;
 using FwdCfg64Causal = FwdCfg<64, 4, 1, false, 4>;
 using FwdCfg64Full = FwdCfg<64, 4, 2, false, 2>;
 
@@ -85,8 +92,18 @@ __global__ __launch_bounds__(C::NT, C::OCC * 4 / C::NW) void fwd_bf16_kernel(
     u16* __restrict__ O, float* __restrict__ LSE, int H, int N, float sl2, int causal,
     const int32_t* __restrict__ kv_len, int nqb, int total) {
   constexpr int BC = C::BC, NT = C::NT, QS = C::QS;
-  __shared__ __attribute__((aligned(16))) u16 Ks[2][BC * C::KSTR];
-  __shared__ __attribute__((aligned(16))) u16 Vs[2][BC * C::VSTR];
+  constexpr bool DL = C::DL;
+  // Register-staged tiles: two buffers per tensor, indexed at run time.
+  __shared__ __attribute__((aligned(16))) u16 Ks[2][DL ? 8 : BC * C::KSTR];
+  __shared__ __attribute__((aligned(16))) u16 Vs[2][DL ? 8 : BC * C::VSTR];
+  // Direct-to-LDS tiles: the two buffers of each tensor are separate arrays
+  // and the loop names them at compile time, so the compiler can tell that
+  // the loads in flight into one buffer do not overlap the reads of the
+  // other and does not make those reads wait for them.
+  __shared__ __attribute__((aligned(16))) u16 Kd0[DL ? BC * C::KSTR : 8];
+  __shared__ __attribute__((aligned(16))) u16 Kd1[DL ? BC * C::KSTR : 8];
+  __shared__ __attribute__((aligned(16))) u16 Vd0[DL ? BC * C::VSTR : 8];
+  __shared__ __attribute__((aligned(16))) u16 Vd1[DL ? BC * C::VSTR : 8];
 
   const int tile = xcd_tile(blockIdx.x, total);
   int qb = tile % nqb;
@@ -164,13 +181,13 @@ __global__ __launch_bounds__(C::NT, C::OCC * 4 / C::NW) void fwd_bf16_kernel(
       *reinterpret_cast<u32x4*>(&Vs[buf][(c / (D / 8)) * C::VSTR + (c % (D / 8)) * 8]) = vreg[rr];
     }
   };
-  // S^T tiles from K buffer `buf` for every slab: rows = keys
+  // S^T tiles from K tile Kt for every slab: rows = keys
   // 32*mt + (8i + 4g + j), column = the slab's query. Each K read serves
   // all QS slabs.
-  auto qk = [&](int buf, f32x16 (*sv)[BC / 32]) {
+  auto qk = [&](const u16* Kt, f32x16 (*sv)[BC / 32]) {
 #pragma unroll
     for (int mt = 0; mt < BC / 32; ++mt) {
-      const u16* kp = &Ks[buf][(32 * mt + r) * C::KSTR + 8 * g];
+      const u16* kp = Kt + (32 * mt + r) * C::KSTR + 8 * g;
       const bf16x8 a0 = ld_lds16(kp);
 #pragma unroll
       for (int s = 0; s < QS; ++s) sv[s][mt] = mfma32_first(a0, qf[s][0]);
@@ -231,7 +248,7 @@ __global__ __launch_bounds__(C::NT, C::OCC * 4 / C::NW) void fwd_bf16_kernel(
   // `buf`: A = V^T rows d = 32t + r, k-slots = keys of chunk c in the order
   // of the score registers (16c + 8h + 4g + 0..3 for slots 4h..4h+3); each
   // V read serves all QS slabs.
-  auto exp_pv = [&](int buf, f32x16 (*sv)[BC / 32]) {
+  auto exp_pv = [&](const u16* Vt, f32x16 (*sv)[BC / 32]) {
     bf16x8 pb[QS][BC / 16];
 #pragma unroll
     for (int s = 0; s < QS; ++s) {
@@ -249,7 +266,7 @@ __global__ __launch_bounds__(C::NT, C::OCC * 4 / C::NW) void fwd_bf16_kernel(
 #pragma unroll
       for (int c = 0; c < BC / 16; ++c) pb[s][c] = pack_bf16x8(sv[s][c >> 1], 8 * (c & 1));
     }
-    const u16* vb = &Vs[buf][v_tr_off];
+    const u16* vb = Vt + v_tr_off;
 #pragma unroll
     for (int t = 0; t < D / 32; ++t)
 #pragma unroll
@@ -262,7 +279,40 @@ __global__ __launch_bounds__(C::NT, C::OCC * 4 / C::NW) void fwd_bf16_kernel(
   };
 
   f32x16 s_cur[QS][BC / 32];
-  if constexpr (C::PIPE) {
+  if constexpr (DL) {
+    // K_j sits in Kd{j%2}, V_j in Vd{j%2}; K runs one tile ahead of V as
+    // below. Each tile's loads go straight to LDS: K_{j+2} into the buffer
+    // K_j left, V_{j+1} into the one V_{j-1} left. Two tiles per trip so
+    // that the buffer names are compile-time constants.
+    if (nt > 0) {
+      tile_to_lds_padded<D, C::KSTR, BC, C::NW>(rK, 0, Kd0, w, lane);
+      tile_to_lds_padded<D, C::VSTR, BC, C::NW>(rV, 0, Vd0, w, lane);
+    }
+    if (nt > 1) tile_to_lds_padded<D, C::KSTR, BC, C::NW>(rK, BC, Kd1, w, lane);
+    wait_vmem_all();
+    __syncthreads();
+    if (nt_w > 0) qk(Kd0, s_cur);
+    __syncthreads();
+    f32x16 s_alt[QS][BC / 32];
+    auto tile = [&](auto odd, int it, f32x16 (*cur)[BC / 32], f32x16 (*nxt)[BC / 32]) {
+      constexpr bool P = decltype(odd)::value;
+      const int kb = it * BC;
+      if (it + 2 < nt) tile_to_lds_padded<D, C::KSTR, BC, C::NW>(rK, kb + 2 * BC, P ? Kd1 : Kd0, w, lane);
+      if (it + 1 < nt) tile_to_lds_padded<D, C::VSTR, BC, C::NW>(rV, kb + BC, P ? Vd0 : Vd1, w, lane);
+      if (it < nt_w) {
+        mask_max(kb, cur);
+        qk(P ? Kd0 : Kd1, nxt);
+        exp_pv(P ? Vd1 : Vd0, cur);
+      }
+      // Each wave waits for its own loads before the barrier publishes them.
+      wait_vmem_all();
+      __syncthreads();
+    };
+    for (int it = 0; it < nt; it += 2) {
+      tile(std::integral_constant<bool, false>{}, it, s_cur, s_alt);
+      if (it + 1 < nt) tile(std::integral_constant<bool, true>{}, it + 1, s_alt, s_cur);
+    }
+  } else if constexpr (C::PIPE) {
     // K runs one tile ahead of V: while tile j's softmax is on the vector
     // ALUs the wave already issues tile j+1's S^T products. K_j sits in
     // Ks[j % 2], V_j in Vs[j % 2]; one barrier per tile.
@@ -277,7 +327,7 @@ __global__ __launch_bounds__(C::NT, C::OCC * 4 / C::NW) void fwd_bf16_kernel(
       store_k(1);
     }
     __syncthreads();
-    if (nt_w > 0) qk(0, s_cur);
+    if (nt_w > 0) qk(Ks[0], s_cur);
     // K_0's buffer is refilled with K_2 during the first tile: every wave
     // must have taken its scores from it first.
     __syncthreads();
@@ -293,8 +343,8 @@ __global__ __launch_bounds__(C::NT, C::OCC * 4 / C::NW) void fwd_bf16_kernel(
         // Next tile's scores (on the last tile this reads a stale buffer and
         // the result is dropped), independent of the softmax below.
         f32x16 s_next[QS][BC / 32];
-        qk((it + 1) & 1, s_next);
-        exp_pv(it & 1, s_cur);
+        qk(Ks[(it + 1) & 1], s_next);
+        exp_pv(Vs[it & 1], s_cur);
 #pragma unroll
         for (int s = 0; s < QS; ++s)
 #pragma unroll
@@ -323,9 +373,9 @@ __global__ __launch_bounds__(C::NT, C::OCC * 4 / C::NW) void fwd_bf16_kernel(
         load_v(kb + BC);
       }
       if (it < nt_w) {
-        qk(it & 1, s_cur);
+        qk(Ks[it & 1], s_cur);
         mask_max(kb, s_cur);
-        exp_pv(it & 1, s_cur);
+        exp_pv(Vs[it & 1], s_cur);
       }
       if (more) {
         store_k((it + 1) & 1);
