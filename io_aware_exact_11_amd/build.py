@@ -37,7 +37,6 @@ _ITER_ILP = ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]
 SOURCE_FLAGS: dict[str, list[str]] = {
     "fa_fwd_d128.hip": _MAX_ILP,
     "fa_bwd_dkdv_d128.hip": _ITER_ILP,
-    "fa_bwd_dq_d128.hip": _MAX_ILP,
 }
 
 

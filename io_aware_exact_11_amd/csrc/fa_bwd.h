@@ -25,6 +25,7 @@
 #pragma once
 
 #include <climits>
+#include <type_traits>
 
 #include "fa_common.h"
 #include "fa_launch.h"
@@ -492,13 +493,19 @@ struct DqCfg {
   static constexpr int NW = 4;
   static constexpr int BR = 32 * NW;           // query rows per workgroup
   static constexpr int BC = 64;                // keys per tile
+  // LDS row strides (elements). K is read row-wise (16-byte reads, 16 rows
+  // per read group) and transposed (4 rows x 4 eight-byte columns): a row
+  // step of 12 banks (mod 64) keeps both conflict-free. V is read row-wise
+  // only: a step of 4 banks.
+  static constexpr int KSTR = D == 128 ? D + 24 : D + 8;
+  static constexpr int VSTR = D + 8;
 };
 
 // dQ for 128 query rows of one (b, h), written once. Shaped like the
 // forward: S^T = K Q^T and dP^T = V dO^T with the wave's Q and dO rows as B
 // operands, so each lane holds one query's P and dS for 32 keys of a tile;
 // dQ^T += K^T dS^T takes dS from those registers and K^T from the same
-// (swizzled) K tile through transposing reads. K and V tiles arrive by
+// (padded) K tile through transposing reads. K and V tiles arrive by
 // direct buffer-to-LDS loads, double-buffered, which keeps the kernel's
 // registers within two waves per SIMD without spilling.
 //
@@ -513,9 +520,15 @@ __global__ __launch_bounds__(256, PRECISE ? 1 : 2) void bwd_dq_kernel(
     float* __restrict__ Dg, float* __restrict__ dQ, int H, int N, float scale, float sl2, int causal,
     const int32_t* __restrict__ kv_len, int nqb, int total) {
   using C = DqCfg<D>;
-  constexpr int BC = C::BC;
-  __shared__ __attribute__((aligned(16))) u16 Ks[2][BC * D];
-  __shared__ __attribute__((aligned(16))) u16 Vs[2][BC * D];
+  constexpr int BC = C::BC, KSTR = C::KSTR, VSTR = C::VSTR;
+  // Tiles arrive by direct-to-LDS loads. The two buffers of each tensor are
+  // separate arrays named at compile time (loop unrolled by two), so the
+  // compiler does not make the reads of one buffer wait for the loads in
+  // flight into the other.
+  __shared__ __attribute__((aligned(16))) u16 K0[BC * KSTR];
+  __shared__ __attribute__((aligned(16))) u16 K1[BC * KSTR];
+  __shared__ __attribute__((aligned(16))) u16 V0[BC * VSTR];
+  __shared__ __attribute__((aligned(16))) u16 V1[BC * VSTR];
 
   const int tile = xcd_tile(blockIdx.x, total);
   int qb = tile % nqb;
@@ -578,30 +591,34 @@ __global__ __launch_bounds__(256, PRECISE ? 1 : 2) void bwd_dq_kernel(
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[t][e] = 0.f;
 
-  auto load = [&](int kb, int buf) {
-    tile_to_lds<D, BC, C::NW>(rK, kb, Ks[buf], w, lane);
-    tile_to_lds<D, BC, C::NW>(rV, kb, Vs[buf], w, lane);
+  auto load = [&](int kb, u16* Kt, u16* Vt) {
+    tile_to_lds_padded<D, KSTR, BC, C::NW>(rK, kb, Kt, w, lane);
+    tile_to_lds_padded<D, VSTR, BC, C::NW>(rV, kb, Vt, w, lane);
   };
   const int tr_row = 4 * g + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
-  if (nt > 0) load(0, 0);
+  if (nt > 0) load(0, K0, V0);
+  wait_vmem_all();
   __syncthreads();
-  for (int it = 0; it < nt; ++it) {
-    const int buf = it & 1;
+  // Tile it: K_it, V_it in buffer it % 2; tile it+1 is loaded into the other.
+  auto step = [&](auto odd, int it) {
+    constexpr bool P = decltype(odd)::value;
+    const u16* Kc = P ? K1 : K0;
+    const u16* Vc = P ? V1 : V0;
     const int kb = it * BC;
-    if (it + 1 < nt) load(kb + BC, buf ^ 1);
+    if (it + 1 < nt) load(kb + BC, P ? K0 : K1, P ? V0 : V1);
     if (it < nt_w) {
       f32x16 s[BC / 32], dp[BC / 32];
 #pragma unroll
       for (int mt = 0; mt < BC / 32; ++mt) {
         const int row = 32 * mt + r;
-        s[mt] = mfma32_first(ld_lds16(&Ks[buf][swz_off<D>(row, 8 * g)]), qf[0]);
-        dp[mt] = mfma32_first(ld_lds16(&Vs[buf][swz_off<D>(row, 8 * g)]), df[0]);
+        s[mt] = mfma32_first(ld_lds16(Kc + row * KSTR + 8 * g), qf[0]);
+        dp[mt] = mfma32_first(ld_lds16(Vc + row * VSTR + 8 * g), df[0]);
 #pragma unroll
         for (int kk = 1; kk < D / 16; ++kk) {
-          s[mt] = mfma32(ld_lds16(&Ks[buf][swz_off<D>(row, 16 * kk + 8 * g)]), qf[kk], s[mt]);
-          dp[mt] = mfma32(ld_lds16(&Vs[buf][swz_off<D>(row, 16 * kk + 8 * g)]), df[kk], dp[mt]);
+          s[mt] = mfma32(ld_lds16(Kc + row * KSTR + 16 * kk + 8 * g), qf[kk], s[mt]);
+          dp[mt] = mfma32(ld_lds16(Vc + row * VSTR + 16 * kk + 8 * g), df[kk], dp[mt]);
         }
       }
       if ((kb + BC > kv_lim) || (causal && kb + BC - 1 > wave_q_first)) {
@@ -636,13 +653,18 @@ __global__ __launch_bounds__(256, PRECISE ? 1 : 2) void bwd_dq_kernel(
 #pragma unroll
         for (int c = 0; c < BC / 16; ++c) {
           const int r0 = 16 * c + tr_row, col = 32 * t + tr_col;
-          const bf16x8 aK = join_tr(ld_lds_tr(&Ks[buf][swz_off<D>(r0, col)]),
-                                    ld_lds_tr(&Ks[buf][swz_off<D>(r0 + 8, col)]));
+          const bf16x8 aK = join_tr(ld_lds_tr(Kc + r0 * KSTR + col), ld_lds_tr(Kc + (r0 + 8) * KSTR + col));
           acc[t] = mfma32(aK, db[c], acc[t]);
           if constexpr (PRECISE) acc[t] = mfma32(aK, dl[c], acc[t]);
         }
     }
+    // Each wave waits for its own loads before the barrier publishes them.
+    wait_vmem_all();
     __syncthreads();
+  };
+  for (int it = 0; it < nt; it += 2) {
+    step(std::integral_constant<bool, false>{}, it);
+    if (it + 1 < nt) step(std::integral_constant<bool, true>{}, it + 1);
   }
 
   if (q < N) {
