@@ -211,10 +211,13 @@ struct DkdvCfg {
   static constexpr int NW = 4;
   static constexpr int BKV = 32 * NW;          // keys per workgroup (32 per wave)
   static constexpr int BQ = 64;                // query rows per block
-  static constexpr int CH = BQ * D / 8 / 256;  // 16-byte chunks per thread per tensor
+  // Q and dO tile row stride (elements): both tiles are read row-wise
+  // (16-byte reads, 16 rows per read group) and transposed (4 rows x 4
+  // eight-byte columns); a row step of 12 banks (d=128) or 52 banks (d=64),
+  // mod 64, keeps both patterns conflict-free.
+  static constexpr int QSTR = D == 128 ? D + 24 : D + 40;
   static constexpr int KCH = BKV * D / 8 / 256;
   static constexpr int DSTR = BKV + 8;         // dS tile row stride (row reads only)
-  static_assert(CH >= 1, "one chunk per thread at least");
 };
 
 // dK, dV for 128 keys of one (b, h). The wave's K and V rows are B operands
@@ -231,8 +234,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   using C = DkdvCfg<D>;
   constexpr int BQ = C::BQ;
   constexpr int NSPLIT = PRECISE ? 2 : 1;
-  __shared__ __attribute__((aligned(16))) u16 Qs[2][BQ * D];
-  __shared__ __attribute__((aligned(16))) u16 dOs[2][BQ * D];
+  constexpr int QSTR = C::QSTR;
+  // Q and dO blocks arrive by direct-to-LDS loads into padded tiles. The two
+  // buffers of each tensor are separate arrays named at compile time (loop
+  // unrolled by two), so the compiler does not make the reads of one buffer
+  // wait for the loads in flight into the other.
+  __shared__ __attribute__((aligned(16))) u16 Q0[BQ * QSTR];
+  __shared__ __attribute__((aligned(16))) u16 Q1[BQ * QSTR];
+  __shared__ __attribute__((aligned(16))) u16 G0[BQ * QSTR];
+  __shared__ __attribute__((aligned(16))) u16 G1[BQ * QSTR];
   __shared__ __attribute__((aligned(16))) float lse2s[2][BQ];
   __shared__ __attribute__((aligned(16))) float Ds[2][BQ];
   // dQ path only: the workgroup's K rows (swizzled) and the dS tile(s).
@@ -295,29 +305,18 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     // (memory counters retire in order) until the block is written to LDS.
     const auto rL = make_rsrc(LSE + (size_t)bh * N, (unsigned)N * 4);
     const auto rD = make_rsrc(Dg + (size_t)bh * N, (unsigned)N * 4);
-    u32x4 qreg[C::CH], oreg[C::CH];
     float lraw = 0.f, draw = 0.f;
     int qrow = 0;
-    auto load = [&](int q0) {
-#pragma unroll
-      for (int rr = 0; rr < C::CH; ++rr) {
-        const int c = tid + 256 * rr;
-        const unsigned off = (unsigned)((q0 + c / (D / 8)) * D + (c % (D / 8)) * 8) * 2;
-        qreg[rr] = ld_buf16(rQ, off);
-        oreg[rr] = ld_buf16(rO, off);
-      }
+    // Block q0: Q and dO rows straight into LDS; this thread's row
+    // statistics raw into registers (scaled when stored).
+    auto load = [&](int q0, u16* Qt, u16* Gt) {
+      tile_to_lds_padded<D, QSTR, BQ, C::NW>(rQ, q0, Qt, w, lane);
+      tile_to_lds_padded<D, QSTR, BQ, C::NW>(rO, q0, Gt, w, lane);
       qrow = q0 + (tid & (BQ - 1));
       lraw = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rL, (unsigned)qrow * 4, 0, 0));
       draw = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rD, (unsigned)qrow * 4, 0, 0));
     };
     auto store = [&](int buf) {
-#pragma unroll
-      for (int rr = 0; rr < C::CH; ++rr) {
-        const int c = tid + 256 * rr;
-        const int off = swz_off<D>(c / (D / 8), (c % (D / 8)) * 8);
-        *reinterpret_cast<u32x4*>(&Qs[buf][off]) = qreg[rr];
-        *reinterpret_cast<u32x4*>(&dOs[buf][off]) = oreg[rr];
-      }
       if (tid < BQ) {
         // rows past N: weight 0 (LSE = +inf) and no D term
         lse2s[buf][tid] = qrow < N ? lraw * kLog2e : INFINITY;
@@ -330,14 +329,18 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const int tr_row = 4 * g + ((lane & 15) >> 2);
     const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
-    load(qb_start * BQ);
+    load(qb_start * BQ, Q0, G0);
+    wait_vmem_all();
     store(0);
     __syncthreads();
-    wait_vmem_all();
-    for (int qb = qb_start; qb < nqb; ++qb) {
+    // Block qb: its tiles in buffer (qb - qb_start) % 2, the next block's
+    // loaded into the other meanwhile.
+    auto step = [&](auto odd, int qb) {
+      constexpr int buf = decltype(odd)::value ? 1 : 0;
+      const u16* Qt = buf ? Q1 : Q0;
+      const u16* Gt = buf ? G1 : G0;
       const int q0 = qb * BQ;
-      const int buf = (qb - qb_start) & 1;
-      if (qb + 1 < nqb) load(q0 + BQ);
+      if (qb + 1 < nqb) load(q0 + BQ, buf ? Q0 : Q1, buf ? G0 : G1);
 
       if ((kw0 < kv_lim) && (!causal || q0 + BQ - 1 >= kw0)) {
         // S = Q K^T, dP = dO V^T: rows = queries 32*qt + 8i + 4g + j, column = key.
@@ -345,12 +348,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 #pragma unroll
         for (int qt = 0; qt < BQ / 32; ++qt) {
           const int row = 32 * qt + r;
-          sa[qt] = mfma32_first(ld_lds16(&Qs[buf][swz_off<D>(row, 8 * g)]), kf[0]);
-          pa[qt] = mfma32_first(ld_lds16(&dOs[buf][swz_off<D>(row, 8 * g)]), vf[0]);
+          sa[qt] = mfma32_first(ld_lds16(Qt + row * QSTR + 8 * g), kf[0]);
+          pa[qt] = mfma32_first(ld_lds16(Gt + row * QSTR + 8 * g), vf[0]);
 #pragma unroll
           for (int kk = 1; kk < D / 16; ++kk) {
-            sa[qt] = mfma32(ld_lds16(&Qs[buf][swz_off<D>(row, 16 * kk + 8 * g)]), kf[kk], sa[qt]);
-            pa[qt] = mfma32(ld_lds16(&dOs[buf][swz_off<D>(row, 16 * kk + 8 * g)]), vf[kk], pa[qt]);
+            sa[qt] = mfma32(ld_lds16(Qt + row * QSTR + 16 * kk + 8 * g), kf[kk], sa[qt]);
+            pa[qt] = mfma32(ld_lds16(Gt + row * QSTR + 16 * kk + 8 * g), vf[kk], pa[qt]);
           }
         }
         // Masked scores become -inf, so their weights come out exactly 0.
@@ -401,10 +404,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 #pragma unroll
           for (int c = 0; c < BQ / 16; ++c) {
             const int r0 = 16 * c + tr_row, col = 32 * t + tr_col;
-            const bf16x8 aO = join_tr(ld_lds_tr(&dOs[buf][swz_off<D>(r0, col)]),
-                                      ld_lds_tr(&dOs[buf][swz_off<D>(r0 + 8, col)]));
-            const bf16x8 aQ = join_tr(ld_lds_tr(&Qs[buf][swz_off<D>(r0, col)]),
-                                      ld_lds_tr(&Qs[buf][swz_off<D>(r0 + 8, col)]));
+            const bf16x8 aO = join_tr(ld_lds_tr(Gt + r0 * QSTR + col), ld_lds_tr(Gt + (r0 + 8) * QSTR + col));
+            const bf16x8 aQ = join_tr(ld_lds_tr(Qt + r0 * QSTR + col), ld_lds_tr(Qt + (r0 + 8) * QSTR + col));
             dv[t] = mfma32(aO, pb[c], dv[t]);
             dk[t] = mfma32(aQ, db[c], dk[t]);
             if constexpr (PRECISE) {
@@ -464,8 +465,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
           }
         }
       }
+      // Each wave waits for its own loads before the barrier publishes them.
+      wait_vmem_all();
       if (qb + 1 < nqb) store(buf ^ 1);
       __syncthreads();
+    };
+    for (int qb = qb_start; qb < nqb; qb += 2) {
+      step(std::integral_constant<bool, false>{}, qb);
+      if (qb + 1 < nqb) step(std::integral_constant<bool, true>{}, qb + 1);
     }
   }
 
@@ -701,25 +708,34 @@ static void launch_dq(const u16* q, const u16* k, const u16* v, const u16* o, co
                      Dws, dQ, s.H, s.N, s.scale, sl2, s.causal, s.kv_len, nqb, total);
 }
 
-// Entry points of the per-head-size translation units.
+// Entry points of the translation units: the key-outer kernel per head
+// size, and (in a unit of its own, compiled with the default scheduler) its
+// variants that also accumulate dQ with atomics.
 template <int D>
-static hipError_t launch_dkdv_any(const BwdArgs& a, const AttnShape& s, bool precise, bool dq_atomic,
-                                  hipStream_t stream) {
+static hipError_t launch_dkdv_default(const BwdArgs& a, const AttnShape& s, bool precise, hipStream_t stream) {
   const float sl2 = s.scale * kLog2e;
   const u16* q = static_cast<const u16*>(a.Q);
   const u16* k = static_cast<const u16*>(a.K);
   const u16* v = static_cast<const u16*>(a.V);
   const u16* g = static_cast<const u16*>(a.dO);
-  if (dq_atomic) {
-    if (precise)
-      launch_dkdv<D, true, true>(q, k, v, g, a.LSE, a.Dws, a.dQ, a.dK, a.dV, s, sl2, stream);
-    else
-      launch_dkdv<D, false, true>(q, k, v, g, a.LSE, a.Dws, a.dQ, a.dK, a.dV, s, sl2, stream);
-  } else if (precise) {
+  if (precise)
     launch_dkdv<D, true, false>(q, k, v, g, a.LSE, a.Dws, a.dQ, a.dK, a.dV, s, sl2, stream);
-  } else {
+  else
     launch_dkdv<D, false, false>(q, k, v, g, a.LSE, a.Dws, a.dQ, a.dK, a.dV, s, sl2, stream);
-  }
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_dkdv_atomic(const BwdArgs& a, const AttnShape& s, bool precise, hipStream_t stream) {
+  const float sl2 = s.scale * kLog2e;
+  const u16* q = static_cast<const u16*>(a.Q);
+  const u16* k = static_cast<const u16*>(a.K);
+  const u16* v = static_cast<const u16*>(a.V);
+  const u16* g = static_cast<const u16*>(a.dO);
+  if (precise)
+    launch_dkdv<D, true, true>(q, k, v, g, a.LSE, a.Dws, a.dQ, a.dK, a.dV, s, sl2, stream);
+  else
+    launch_dkdv<D, false, true>(q, k, v, g, a.LSE, a.Dws, a.dQ, a.dK, a.dV, s, sl2, stream);
   return hipGetLastError();
 }
 

@@ -59,14 +59,15 @@ hipError_t launch_bwd_bf16(const void* Q, const void* K, const void* V, const vo
     // dK/dV kernel, which therefore runs second.
     e = d64 ? launch_dq_bf16_d64(a, s, false, stream) : launch_dq_bf16_d128(a, s, false, stream);
     if (e != hipSuccess) return e;
-    return d64 ? launch_dkdv_bf16_d64(a, s, false, false, stream)
-               : launch_dkdv_bf16_d128(a, s, false, false, stream);
+    return d64 ? launch_dkdv_bf16_d64(a, s, false, stream) : launch_dkdv_bf16_d128(a, s, false, stream);
   }
   e = d64 ? launch_row_term<64>(a, s, precise, stream) : launch_row_term<128>(a, s, precise, stream);
   if (e != hipSuccess) return e;
-  e = d64 ? launch_dkdv_bf16_d64(a, s, precise, dq_atomic, stream)
-          : launch_dkdv_bf16_d128(a, s, precise, dq_atomic, stream);
-  if (e != hipSuccess || dq_atomic) return e;
+  if (dq_atomic)
+    return d64 ? launch_dkdv_atomic_bf16_d64(a, s, precise, stream)
+               : launch_dkdv_atomic_bf16_d128(a, s, precise, stream);
+  e = d64 ? launch_dkdv_bf16_d64(a, s, precise, stream) : launch_dkdv_bf16_d128(a, s, precise, stream);
+  if (e != hipSuccess) return e;
   return d64 ? launch_dq_bf16_d64(a, s, precise, stream) : launch_dq_bf16_d128(a, s, precise, stream);
 }
 

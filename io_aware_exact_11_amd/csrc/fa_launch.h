@@ -33,10 +33,10 @@ hipError_t launch_fwd_bf16_d64(const void* Q, const void* K, const void* V, void
                                const AttnShape& s, hipStream_t stream);
 hipError_t launch_fwd_bf16_d128(const void* Q, const void* K, const void* V, void* O, float* LSE,
                                 const AttnShape& s, hipStream_t stream);
-hipError_t launch_dkdv_bf16_d64(const BwdArgs& a, const AttnShape& s, bool precise, bool dq_atomic,
-                                hipStream_t stream);
-hipError_t launch_dkdv_bf16_d128(const BwdArgs& a, const AttnShape& s, bool precise, bool dq_atomic,
-                                 hipStream_t stream);
+hipError_t launch_dkdv_bf16_d64(const BwdArgs& a, const AttnShape& s, bool precise, hipStream_t stream);
+hipError_t launch_dkdv_bf16_d128(const BwdArgs& a, const AttnShape& s, bool precise, hipStream_t stream);
+hipError_t launch_dkdv_atomic_bf16_d64(const BwdArgs& a, const AttnShape& s, bool precise, hipStream_t stream);
+hipError_t launch_dkdv_atomic_bf16_d128(const BwdArgs& a, const AttnShape& s, bool precise, hipStream_t stream);
 hipError_t launch_dq_bf16_d64(const BwdArgs& a, const AttnShape& s, bool precise, hipStream_t stream);
 hipError_t launch_dq_bf16_d128(const BwdArgs& a, const AttnShape& s, bool precise, hipStream_t stream);
 
