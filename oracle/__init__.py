@@ -5,5 +5,6 @@ import this package; the library never does.
 """
 from .attention import (  # noqa: F401
     fp32_scale, visible_mask, head_forward, head_backward, forward, backward,
-    forward_rows, online_softmax, blockwise_attention_row,
+    forward_rows, online_softmax, blockwise_attention_row, decode_visible_mask,
+    decode_head_forward, decode_forward,
 )

@@ -34,8 +34,16 @@ Memory", chapter 08) and ``blockwise_attention_row`` (tiles of keys with the
 output rescaled by e^(m_old - m_new), chapter 08, and "FlashAttention does
 more arithmetic to move less data", the four moves).
 
-Every function here is pinned by tests/test_oracle_pins.py; none is
-"parity unpinned".
+Decoding ("FlashAttention — why it mattered", the closing note that
+token-by-token decoding has one new query at a time and is limited by
+reading the cached keys and values): ``decode_head_forward`` takes n_q new
+queries against a cache of n_k key slots of which the first kv_len hold
+keys. Reading (the pages do not define it): the queries are the last n_q
+positions of that sequence, so with causal masking query i sees keys
+j <= kv_len - n_q + i (bottom-right alignment); without it, all j < kv_len.
+
+Every function here is pinned by tests/test_oracle_pins.py and
+tests/test_oracle_decode.py; none is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -44,6 +52,7 @@ import numpy as np
 __all__ = [
     "fp32_scale", "visible_mask", "head_forward", "head_backward", "forward",
     "backward", "forward_rows", "online_softmax", "blockwise_attention_row",
+    "decode_visible_mask", "decode_head_forward", "decode_forward",
 ]
 
 
@@ -194,3 +203,46 @@ def blockwise_attention_row(qi, k, v, scale, block):
         acc = alpha * acc + p @ v[start:start + block]
         m = m_new
     return acc / ell, m + np.log(ell)
+
+
+def decode_visible_mask(n_q: int, n_k: int, kv_len=None, causal: bool = False) -> np.ndarray:
+    """Boolean [n_q, n_k] for n_q new queries against n_k cache slots.
+
+    The first L = kv_len (or n_k) slots hold keys. Without causal masking
+    every query sees keys j < L; with it, query i is position L - n_q + i of
+    the sequence and sees keys j <= L - n_q + i.
+    """
+    L = n_k if kv_len is None else max(0, min(int(kv_len), n_k))
+    cols = np.arange(n_k)[None, :]
+    vis = np.broadcast_to(cols < L, (n_q, n_k)).copy()
+    if causal:
+        vis &= cols <= (L - n_q + np.arange(n_q))[:, None]
+    return vis
+
+
+def decode_head_forward(q, k, v, scale, kv_len=None, causal=False):
+    """n_q queries against one head's key/value cache, in float64.
+
+    q: [n_q, d]; k, v: [n_k, d]. Returns (O [n_q, d], LSE [n_q]) with the
+    same softmax, log-sum-exp and fully-masked-row conventions as
+    ``head_forward``.
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    s = fp32_scale(scale)
+    S = s * (q @ k.T)
+    P, lse = _softmax_rows(S, decode_visible_mask(q.shape[0], k.shape[0], kv_len, causal))
+    return P @ v, lse
+
+
+def decode_forward(Q, K, V, scale, kv_len=None, causal=False):
+    """Q [B, H, n_q, d], K and V [B, H, n_k, d] -> (O [B, H, n_q, d], LSE [B, H, n_q]) float64."""
+    B, H, n_q, d = Q.shape
+    O = np.empty((B, H, n_q, d), np.float64)
+    LSE = np.empty((B, H, n_q), np.float64)
+    for b in range(B):
+        L = None if kv_len is None else int(kv_len[b])
+        for h in range(H):
+            O[b, h], LSE[b, h] = decode_head_forward(Q[b, h], K[b, h], V[b, h], scale, L, causal)
+    return O, LSE
