@@ -116,6 +116,31 @@ int flash_attn_bwd_f32(const float* Q, const float* K, const float* V, const flo
                        int B, int H, int N, int d, float scale, int causal,
                        const int32_t* kv_len, unsigned flags, void* stream);
 
+/*
+ * Decoding forward, bf16: Nq new queries per (b, h) against a key/value
+ * cache ("FlashAttention — why it mattered": token-by-token decoding has
+ * one new query at a time and is limited by reading the cache).
+ *   Q:   bf16 [B,H,Nq,d], the new queries (1 <= Nq <= 8, Nq <= Nk);
+ *   K,V: bf16 [B,H,Nk,d], the cache; slots j < kv_len[b] (all Nk when
+ *        kv_len is NULL; values clamped to [0, Nk]) hold keys;
+ *   O:   bf16 [B,H,Nq,d] output; LSE: float [B,H,Nq] output, natural log.
+ * Query i may see key j iff j < L_b and, when causal != 0, j <= L_b - Nq + i
+ * (the queries are the last Nq positions of the sequence). A query that
+ * sees no key gets O = 0 and LSE = -inf. Scores, softmax statistics and the
+ * output accumulate in fp32. The keys are processed in chunks whose partial
+ * results are merged with the running-softmax rule ("FlashAttention and GPU
+ * Memory", chapter 08); workspace (device, 256-byte aligned, at least
+ * flash_attn_decode_workspace_bytes(...) bytes, contents on entry do not
+ * matter) holds the per-chunk results. Nq > 8 or d outside {64, 128} is
+ * FA_ERR_UNSUPPORTED; other conventions as above.
+ */
+int flash_attn_decode_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                          void* workspace, size_t workspace_bytes, int B, int H, int Nq, int Nk,
+                          int d, float scale, int causal, const int32_t* kv_len, void* stream);
+
+/* Workspace bytes flash_attn_decode_fwd needs (0 for bad sizes). */
+size_t flash_attn_decode_workspace_bytes(int B, int H, int Nq, int Nk, int d);
+
 /* Static, human-readable name of a status code. */
 const char* flash_attn_status_string(int status);
 

@@ -21,7 +21,8 @@ FA_BWD_PRECISE = 1
 FA_BWD_DQ_ATOMIC = 2
 
 EXPORTED = ("flash_attn_fwd", "flash_attn_bwd", "flash_attn_bwd_workspace_bytes",
-            "flash_attn_fwd_f32", "flash_attn_bwd_f32", "flash_attn_status_string")
+            "flash_attn_fwd_f32", "flash_attn_bwd_f32", "flash_attn_decode_fwd",
+            "flash_attn_decode_workspace_bytes", "flash_attn_status_string")
 
 
 class FlashAttnError(RuntimeError):
@@ -53,6 +54,10 @@ def load_library():
         fn.restype = ctypes.c_int
     lib.flash_attn_bwd_workspace_bytes.argtypes = [i, i, i, i, u]
     lib.flash_attn_bwd_workspace_bytes.restype = sz
+    lib.flash_attn_decode_fwd.argtypes = [p, p, p, p, p, p, sz, i, i, i, i, i, f, i, p, p]
+    lib.flash_attn_decode_fwd.restype = ctypes.c_int
+    lib.flash_attn_decode_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.flash_attn_decode_workspace_bytes.restype = sz
     lib.flash_attn_status_string.argtypes = [i]
     lib.flash_attn_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -170,3 +175,37 @@ def flash_attn_bwd_f32(q, k, v, o, do, lse, causal=False, scale=None, kv_len=Non
     """fp32 backward: returns fp32 (dQ, dK, dV)."""
     return _bwd("flash_attn_bwd_f32", torch.float32, q, k, v, o, do, lse, causal, scale, kv_len, 0,
                 dq, dk, dv, workspace)
+
+
+def flash_attn_decode_workspace_bytes(B: int, H: int, Nq: int, Nk: int, d: int) -> int:
+    return int(load_library().flash_attn_decode_workspace_bytes(B, H, Nq, Nk, d))
+
+
+def flash_attn_decode_fwd(q, k, v, causal=False, scale=None, kv_len=None, out=None, lse=None,
+                          workspace=None):
+    """bf16 decoding forward: q [B,H,Nq,d] against the cache k, v [B,H,Nk,d].
+
+    Returns (O bf16 [B,H,Nq,d], LSE fp32 [B,H,Nq])."""
+    lib = load_library()
+    _check("q", q, torch.bfloat16, q.shape)
+    _check("k", k, torch.bfloat16, k.shape)
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k must be [B, H, N, d]")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    _check("k", k, torch.bfloat16, (B, H, Nk, d))
+    _check("v", v, torch.bfloat16, (B, H, Nk, d))
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check("out", out, torch.bfloat16, q.shape)
+    _check("lse", lse, torch.float32, (B, H, Nq))
+    need = flash_attn_decode_workspace_bytes(B, H, Nq, Nk, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    kv_len = _kv(kv_len, B, q.device)
+    st = lib.flash_attn_decode_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), B, H, Nq, Nk, d,
+                                   _scale(scale, d), int(bool(causal)), _ptr(kv_len), _stream())
+    if st != FA_OK:
+        raise FlashAttnError(st, "flash_attn_decode_fwd")
+    return out, lse

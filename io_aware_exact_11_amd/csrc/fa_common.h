@@ -8,6 +8,7 @@ namespace fa {
 
 typedef unsigned short u16;
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __bf16 __attribute__((ext_vector_type(2))) bf16x2;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
@@ -78,6 +79,15 @@ __device__ __forceinline__ u32x4 ld_global16(const void* p) {
 
 __device__ __forceinline__ bf16x8 ld_lds16(const u16* p) {
   return *reinterpret_cast<const bf16x8*>(p);
+}
+
+// A 32-bit word as two bf16 values (low half first). Written with memcpy:
+// __builtin_bit_cast applied to an element of a vector value was compiled
+// as a cast of the vector's first element.
+__device__ __forceinline__ bf16x2 as_bf16x2(unsigned x) {
+  bf16x2 r;
+  __builtin_memcpy(&r, &x, sizeof(r));
+  return r;
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -46,6 +46,21 @@ hipError_t launch_bwd_bf16(const void* Q, const void* K, const void* V, const vo
                            float* Dws, const AttnShape& s, bool precise, bool dq_atomic,
                            hipStream_t stream);
 
+// Decoding: Nq new queries per (b, h) against Nk cache slots.
+struct DecodeShape {
+  int B, H, Nq, Nk, d;
+  float scale;
+  int causal;
+  const int32_t* kv_len;  // device [B] or nullptr
+};
+
+// Key chunks per (b, h); the workspace holds, per chunk and query, d fp32
+// output values and one log-sum-exp.
+int decode_chunks(int nk);
+
+hipError_t launch_decode_bf16(const void* Q, const void* K, const void* V, void* O, float* LSE, float* ws,
+                              const DecodeShape& s, hipStream_t stream);
+
 hipError_t launch_fwd_f32(const float* Q, const float* K, const float* V, float* O, float* LSE,
                           const AttnShape& s, hipStream_t stream);
 

@@ -90,6 +90,11 @@ int bwd_common(const void* Q, const void* K, const void* V, const void* O, const
   return check_ptrs(in, in_p, 6, out, out_p, 4);
 }
 
+size_t decode_ws_bytes(int B, int H, int Nq, int Nk, int d) {
+  const size_t slots = (size_t)B * H * fa::decode_chunks(Nk) * Nq;
+  return (slots * (size_t)(d + 1) * sizeof(float) + 255) & ~(size_t)255;
+}
+
 int hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 
 }  // namespace
@@ -144,6 +149,37 @@ int flash_attn_bwd_f32(const float* Q, const float* K, const float* V, const flo
   const fa::AttnShape s{B, H, N, d, scale, causal, kv_len};
   return hip_status(fa::launch_bwd_f32(Q, K, V, O, dO, LSE, dQ, dK, dV, static_cast<float*>(workspace),
                                        s, static_cast<hipStream_t>(stream)));
+}
+
+size_t flash_attn_decode_workspace_bytes(int B, int H, int Nq, int Nk, int d) {
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1) return 0;
+  return decode_ws_bytes(B, H, Nq, Nk, d);
+}
+
+int flash_attn_decode_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, void* workspace,
+                          size_t workspace_bytes_, int B, int H, int Nq, int Nk, int d, float scale,
+                          int causal, const int32_t* kv_len, void* stream) {
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1) return FA_ERR_INVALID_ARG;
+  if (!isfinite(scale) || !(scale > 0.f)) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  if (Nq > Nk) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (Nq > 8) return FA_ERR_UNSUPPORTED;
+  if ((int64_t)B * H * Nk * d > INT32_MAX) return FA_ERR_UNSUPPORTED;
+  const size_t need = decode_ws_bytes(B, H, Nq, Nk, d);
+  if (workspace_bytes_ < need) return FA_ERR_INVALID_ARG;
+  const size_t qbytes = (size_t)B * H * Nq * d * 2;
+  const size_t kbytes = (size_t)B * H * Nk * d * 2;
+  const size_t lbytes = (size_t)B * H * Nq * sizeof(float);
+  const void* in_p[3] = {Q, K, V};
+  const Span in[3] = {span(Q, qbytes), span(K, kbytes), span(V, kbytes)};
+  const void* out_p[3] = {O, LSE, workspace};
+  const Span out[3] = {span(O, qbytes), span(LSE, lbytes), span(workspace, need)};
+  const int st = check_ptrs(in, in_p, 3, out, out_p, 3);
+  if (st != FA_OK) return st;
+  const fa::DecodeShape s{B, H, Nq, Nk, d, scale, causal, kv_len};
+  return hip_status(fa::launch_decode_bf16(Q, K, V, O, LSE, static_cast<float*>(workspace), s,
+                                           static_cast<hipStream_t>(stream)));
 }
 
 const char* flash_attn_status_string(int status) {

@@ -15,6 +15,10 @@ seed):
      (b, h), uniform over the valid keys, whose K row is multiplied by 8;
   4. bf16 workloads round every tensor to bfloat16 with round-to-nearest-even.
 
+Decoding inputs (``make_decode_inputs``) follow the same recipe with Q of
+shape [B, H, Nq, d] and K, V of shape [B, H, Nk, d] (no dO), then, when
+ragged, one cache length per batch row kv_len[b] ~ U{Nk/2 .. Nk}.
+
 The shapes follow the pages' workloads: the GPT-2-medium attention shape
 (FlashAttention does more arithmetic to move less data, section
 "FlashAttention never writes the full score table to HBM"), the N=4096,
@@ -106,6 +110,30 @@ def make_inputs(B: int, H: int, N: int, d: int, seed: int, dtype: str = "bf16",
             out[name] = bf16_bits_to_f32(bits)
     elif dtype != "fp32":
         raise ValueError(f"unknown dtype {dtype!r}")
+    return out
+
+
+# Decoding workload: one new query per head against a long key/value cache
+# (the token-by-token decoding of "FlashAttention — why it mattered"), with
+# the GPT-style width of 32 heads of 128 and a 32K-slot cache per sequence.
+DECODE_WORKLOADS = {
+    "decode_32k": dict(B=8, H=32, Nq=1, Nk=32768, d=128, causal=False, ragged=False, seed=6),
+}
+
+
+def make_decode_inputs(B: int, H: int, Nq: int, Nk: int, d: int, seed: int, ragged: bool = False) -> dict:
+    """Q [B,H,Nq,d], K and V [B,H,Nk,d] (bf16 values as float32 plus "_bits"),
+    and "kv_len" (int32 [B], ragged) or None."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = {"Q": rng.standard_normal(size=(B, H, Nq, d), dtype=np.float32)}
+    for name in ("K", "V"):
+        out[name] = rng.standard_normal(size=(B, H, Nk, d), dtype=np.float32)
+    out["kv_len"] = (rng.integers(Nk // 2, Nk, endpoint=True, size=B).astype(np.int32)
+                     if ragged else None)
+    for name in ("Q", "K", "V"):
+        bits = bf16_round_bits(out[name])
+        out[name + "_bits"] = bits
+        out[name] = bf16_bits_to_f32(bits)
     return out
 
 

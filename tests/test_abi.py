@@ -119,3 +119,42 @@ def test_binding_fails_loudly_without_gpu_tensors():
     x = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         fa.flash_attn_fwd(x, x, x)
+
+
+def test_decode_workspace_bytes(lib):
+    # one chunk of 512 keys: per (b, h, chunk, query) d + 1 floats
+    assert fa.flash_attn_decode_workspace_bytes(2, 3, 1, 512, 64) == ((2 * 3 * 1 * 1 * 65 * 4 + 255) // 256) * 256
+    assert fa.flash_attn_decode_workspace_bytes(1, 1, 4, 1025, 128) == ((3 * 4 * 129 * 4 + 255) // 256) * 256
+    assert fa.flash_attn_decode_workspace_bytes(1, 1, 0, 16, 64) == 0
+
+
+def _dec(lib, B=1, H=1, Nq=1, Nk=64, d=64, scale=0.125, causal=0, ws=None, ptrs=None):
+    span = B * H * Nk * d * 2 + 4096
+    step = (span + 4095) // 4096 * 4096
+    base = [FAKE + i * step for i in range(6)]  # Q, K, V, O, LSE, workspace
+    if ptrs:
+        base = [ptrs.get(i, b) for i, b in enumerate(base)]
+    wsb = fa.flash_attn_decode_workspace_bytes(B, H, Nq, Nk, d) if ws is None else ws
+    args = [ctypes.c_void_p(p) if p is not None else None for p in base]
+    return lib.flash_attn_decode_fwd(*args, wsb, B, H, Nq, Nk, d, scale, causal, None, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), fa.binding.FA_ERR_INVALID_ARG),
+    (dict(Nq=0), fa.binding.FA_ERR_INVALID_ARG),
+    (dict(Nk=0), fa.binding.FA_ERR_INVALID_ARG),
+    (dict(Nq=9, Nk=64), fa.binding.FA_ERR_UNSUPPORTED),
+    (dict(Nq=5, Nk=4), fa.binding.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.binding.FA_ERR_UNSUPPORTED),
+    (dict(scale=0.0), fa.binding.FA_ERR_INVALID_ARG),
+    (dict(scale=math.nan), fa.binding.FA_ERR_INVALID_ARG),
+    (dict(causal=3), fa.binding.FA_ERR_INVALID_ARG),
+    (dict(ws=16), fa.binding.FA_ERR_INVALID_ARG),
+    (dict(B=4096, H=64, Nk=8192, d=128), fa.binding.FA_ERR_UNSUPPORTED),
+    (dict(ptrs={0: None}), fa.binding.FA_ERR_INVALID_ARG),
+    (dict(ptrs={5: None}), fa.binding.FA_ERR_INVALID_ARG),          # NULL workspace
+    (dict(ptrs={3: FAKE}), fa.binding.FA_ERR_INVALID_ARG),          # O aliases Q
+    (dict(ptrs={4: FAKE + 4}), fa.binding.FA_ERR_INVALID_ARG),      # misaligned LSE
+])
+def test_decode_rejects(lib, kw, status):
+    assert _dec(lib, **kw) == status
