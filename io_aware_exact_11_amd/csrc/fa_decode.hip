@@ -33,7 +33,9 @@ struct DecCfg {
   static constexpr int LPK = D / 8;             // lanes per key row
   static constexpr int KPI = 64 / LPK;          // rows per wave load
   static constexpr int KPW = kDecChunk / NW;    // keys per wave
-  static constexpr int UNROLL = 4;              // loads per tensor in flight
+  // Loads per tensor in flight: fewer for more queries, whose per-query
+  // state would otherwise push the kernel below two waves per SIMD.
+  static constexpr int UNROLL = NQ >= 8 ? 1 : (NQ >= 4 ? 2 : 4);
   static constexpr int ITER = KPW / (KPI * UNROLL);
   static_assert(ITER * KPI * UNROLL == KPW, "chunk split");
 };
