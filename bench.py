@@ -12,7 +12,9 @@ pair backward (recomputed S, dP, dV, dK, dQ), 14 d per pair for a step.
 
 The primary workload is the GPT-2-medium attention shape (B=64, H=16,
 N=1024, d=64, causal); the N=4096 and N=16384 head-dim-128 workloads are
-timed the same way and reported under "workloads". Only one GPU is used.
+timed the same way and reported under "workloads", next to the decoding
+forward (one new query per head against a 32K-slot cache), which is
+memory-bound and reported as an HBM rate. Only one GPU is used.
 """
 from __future__ import annotations
 
@@ -27,6 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 matrix-core peak (2.5 PFLOP/s class)
+PEAK_HBM_TBPS = 8.0        # MI355X HBM3E peak
 PRIMARY = "gpt2_medium"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -150,6 +153,41 @@ def cpu_baseline(name, causal, budget_s=10.0):
             "seconds": round(dt, 2)}
 
 
+def decode_case(steps, warmup):
+    """The decoding forward on the 32K-slot cache workload: time per call
+    from events on the stream, and the HBM rate of its algorithmic bytes
+    (K and V read once, Q read, O and LSE written)."""
+    import torch
+    import io_aware_exact_11_amd as fa
+    from io_aware_exact_11_amd import workloads as wl
+    name = "decode_32k"
+    c = wl.DECODE_WORKLOADS[name]
+    B, H, Nq, Nk, d = c["B"], c["H"], c["Nq"], c["Nk"], c["d"]
+    x = wl.make_decode_inputs(B, H, Nq, Nk, d, c["seed"], c["ragged"])
+    dev = lambda bits: torch.from_numpy(bits.view("int16")).view(torch.bfloat16).cuda()
+    q, k, v = (dev(x[n + "_bits"]) for n in ("Q", "K", "V"))
+    del x
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device="cuda")
+    ws = torch.empty(fa.flash_attn_decode_workspace_bytes(B, H, Nq, Nk, d), dtype=torch.uint8, device="cuda")
+    scale = float(d) ** -0.5
+    for _ in range(warmup):
+        fa.flash_attn_decode_fwd(q, k, v, causal=c["causal"], scale=scale, out=o, lse=lse, workspace=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        fa.flash_attn_decode_fwd(q, k, v, causal=c["causal"], scale=scale, out=o, lse=lse, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    nbytes = 2 * B * H * Nk * d * 2 + 2 * B * H * Nq * d * 2 + B * H * Nq * 4
+    gbps = nbytes / (us * 1e-6) / 1e9
+    return {"workload": name, "kind": "decode forward", "B": B, "H": H, "Nq": Nq, "Nk": Nk, "d": d,
+            "us_per_call": round(us, 2), "hbm_gbps": round(gbps, 1),
+            "hbm_frac": round(gbps / (PEAK_HBM_TBPS * 1e3), 4), "algorithmic_bytes": nbytes}
+
+
 def memory_sweep():
     """Peak device memory of one fwd+bwd step (inputs, outputs, workspace) at
     B=2, H=16, d=128, causal, for growing N: grows linearly in N."""
@@ -259,6 +297,7 @@ def main():
                           "fwd_bwd_frac": round((cf + cb) / (wms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)})
             del c
             torch.cuda.empty_cache()
+        extra.append(decode_case(args.steps, args.warmup))
         result["workloads"] = extra
         result["memory_sweep_B2_H16_d128_causal"] = memory_sweep()
 
