@@ -141,6 +141,43 @@ int flash_attn_decode_fwd(const void* Q, const void* K, const void* V, void* O, 
 /* Workspace bytes flash_attn_decode_fwd needs (0 for bad sizes). */
 size_t flash_attn_decode_workspace_bytes(int B, int H, int Nq, int Nk, int d);
 
+/* Fused dropout ("FlashAttention and GPU Memory", chapter 07 Blocks, lists
+ * dropout among the steps fused into one kernel; chapter 09 has the
+ * backward regenerate the dropout mask from the generator state instead of
+ * storing it). The mask is never written to memory by these two calls.
+ *
+ * Each weight P_ij of the softmax is kept with probability (256 - t)/256,
+ * t = round(256 * p_drop), and kept weights are scaled by 256/(256 - t):
+ * O = (P o Z * 256/(256 - t)) V, so the expected output is exact attention.
+ * LSE is the log-sum-exp of the undropped scores, as in flash_attn_fwd.
+ * Z comes from Philox4x32-10 (Salmon et al., SC 2011) keyed by `seed`
+ * (low word, high word) with counter (j/4, i/4, b*H + h, offset) for query
+ * i and key j: element (i, j) is kept iff byte j%4 of output word i%4 is
+ * >= t. The same (seed, offset) must be passed to the backward; a new
+ * offset draws an independent mask with the same seed.
+ *
+ * p_drop must satisfy 0 <= p_drop < 1 and round(256 p_drop) < 256,
+ * otherwise FA_ERR_INVALID_ARG. bf16 tensors only; other arguments and
+ * conventions as flash_attn_fwd / flash_attn_bwd. The backward accepts
+ * FA_BWD_PRECISE (any other flag is FA_ERR_INVALID_ARG) and the workspace
+ * of flash_attn_bwd_workspace_bytes(B, H, N, d, flags).
+ */
+int flash_attn_fwd_dropout(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
+                           int N, int d, float scale, int causal, const int32_t* kv_len, float p_drop,
+                           uint64_t seed, uint32_t offset, void* stream);
+
+int flash_attn_bwd_dropout(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                           const float* LSE, float* dQ, float* dK, float* dV, void* workspace,
+                           size_t workspace_bytes, int B, int H, int N, int d, float scale, int causal,
+                           const int32_t* kv_len, float p_drop, uint64_t seed, uint32_t offset, unsigned flags,
+                           void* stream);
+
+/* Writes the keep mask the two calls above use, as bytes (1 = kept), to the
+ * DEVICE array mask[B][H][N_q][N_k] (caller-owned, B*H*N_q*N_k bytes), for
+ * inspection and testing. Same p_drop, seed and offset rules; N_q, N_k >= 1. */
+int flash_attn_dropout_mask(uint8_t* mask, int B, int H, int N_q, int N_k, float p_drop, uint64_t seed,
+                            uint32_t offset, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* flash_attn_status_string(int status);
 

@@ -22,7 +22,8 @@ FA_BWD_DQ_ATOMIC = 2
 
 EXPORTED = ("flash_attn_fwd", "flash_attn_bwd", "flash_attn_bwd_workspace_bytes",
             "flash_attn_fwd_f32", "flash_attn_bwd_f32", "flash_attn_decode_fwd",
-            "flash_attn_decode_workspace_bytes", "flash_attn_status_string")
+            "flash_attn_decode_workspace_bytes", "flash_attn_fwd_dropout", "flash_attn_bwd_dropout",
+            "flash_attn_dropout_mask", "flash_attn_status_string")
 
 
 class FlashAttnError(RuntimeError):
@@ -58,6 +59,13 @@ def load_library():
     lib.flash_attn_decode_fwd.restype = ctypes.c_int
     lib.flash_attn_decode_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.flash_attn_decode_workspace_bytes.restype = sz
+    u64 = ctypes.c_uint64
+    lib.flash_attn_fwd_dropout.argtypes = fwd_args[:-1] + [f, u64, u, p]
+    lib.flash_attn_fwd_dropout.restype = ctypes.c_int
+    lib.flash_attn_bwd_dropout.argtypes = bwd_args[:-2] + [f, u64, u, u, p]
+    lib.flash_attn_bwd_dropout.restype = ctypes.c_int
+    lib.flash_attn_dropout_mask.argtypes = [p, i, i, i, i, f, u64, u, p]
+    lib.flash_attn_dropout_mask.restype = ctypes.c_int
     lib.flash_attn_status_string.argtypes = [i]
     lib.flash_attn_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -104,7 +112,7 @@ def _scale(scale, d):
     return float(d) ** -0.5 if scale is None else float(scale)
 
 
-def _fwd(name, dtype, q, k, v, causal, scale, kv_len, out, lse):
+def _fwd(name, dtype, q, k, v, causal, scale, kv_len, out, lse, extra=()):
     lib = load_library()
     _check("q", q, dtype, q.shape)
     if q.dim() != 4:
@@ -118,13 +126,13 @@ def _fwd(name, dtype, q, k, v, causal, scale, kv_len, out, lse):
     _check("lse", lse, torch.float32, (B, H, N))
     kv_len = _kv(kv_len, B, q.device)
     st = getattr(lib, name)(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d,
-                            _scale(scale, d), int(bool(causal)), _ptr(kv_len), _stream())
+                            _scale(scale, d), int(bool(causal)), _ptr(kv_len), *extra, _stream())
     if st != FA_OK:
         raise FlashAttnError(st, name)
     return out, lse
 
 
-def _bwd(name, dtype, q, k, v, o, do, lse, causal, scale, kv_len, flags, dq, dk, dv, workspace):
+def _bwd(name, dtype, q, k, v, o, do, lse, causal, scale, kv_len, flags, dq, dk, dv, workspace, extra=None):
     lib = load_library()
     _check("q", q, dtype, q.shape)
     if q.dim() != 4:
@@ -143,9 +151,10 @@ def _bwd(name, dtype, q, k, v, o, do, lse, causal, scale, kv_len, flags, dq, dk,
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     kv_len = _kv(kv_len, B, q.device)
+    tail = (int(flags),) if extra is None else tuple(extra)
     st = getattr(lib, name)(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
                             _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel() * workspace.element_size(),
-                            B, H, N, d, _scale(scale, d), int(bool(causal)), _ptr(kv_len), int(flags),
+                            B, H, N, d, _scale(scale, d), int(bool(causal)), _ptr(kv_len), *tail,
                             _stream())
     if st != FA_OK:
         raise FlashAttnError(st, name)
@@ -209,3 +218,33 @@ def flash_attn_decode_fwd(q, k, v, causal=False, scale=None, kv_len=None, out=No
     if st != FA_OK:
         raise FlashAttnError(st, "flash_attn_decode_fwd")
     return out, lse
+
+
+def _drop_args(p_drop, seed, offset):
+    return (float(p_drop), int(seed) & 0xFFFFFFFFFFFFFFFF, int(offset) & 0xFFFFFFFF)
+
+
+def flash_attn_fwd_dropout(q, k, v, p_drop, seed, offset=0, causal=False, scale=None, kv_len=None, out=None,
+                           lse=None):
+    """bf16 forward with fused dropout: returns (O bf16, LSE fp32 of the undropped scores)."""
+    return _fwd("flash_attn_fwd_dropout", torch.bfloat16, q, k, v, causal, scale, kv_len, out, lse,
+                _drop_args(p_drop, seed, offset))
+
+
+def flash_attn_bwd_dropout(q, k, v, o, do, lse, p_drop, seed, offset=0, causal=False, scale=None, kv_len=None,
+                           precise=False, dq=None, dk=None, dv=None, workspace=None):
+    """bf16 backward with the dropout mask regenerated: returns fp32 (dQ, dK, dV)."""
+    flags = FA_BWD_PRECISE if precise else 0
+    return _bwd("flash_attn_bwd_dropout", torch.bfloat16, q, k, v, o, do, lse, causal, scale, kv_len, flags,
+                dq, dk, dv, workspace, _drop_args(p_drop, seed, offset) + (flags,))
+
+
+def flash_attn_dropout_mask(B, H, N_q, N_k, p_drop, seed, offset=0, out=None, device="cuda"):
+    """The keep mask of the dropout calls as uint8 [B, H, N_q, N_k] (1 = kept)."""
+    lib = load_library()
+    out = torch.empty((B, H, N_q, N_k), dtype=torch.uint8, device=device) if out is None else out
+    _check("out", out, torch.uint8, (B, H, N_q, N_k))
+    st = lib.flash_attn_dropout_mask(_ptr(out), B, H, N_q, N_k, *_drop_args(p_drop, seed, offset), _stream())
+    if st != FA_OK:
+        raise FlashAttnError(st, "flash_attn_dropout_mask")
+    return out

@@ -28,6 +28,7 @@
 #include <type_traits>
 
 #include "fa_common.h"
+#include "fa_dropout.h"
 #include "fa_launch.h"
 
 namespace fa {
@@ -81,11 +82,14 @@ struct ExactDCfg {
   static constexpr int KCH = BC * D / 8 / 256;
 };
 
-template <int D>
+// DROP: dP of kept elements is scaled by the keep factor, dropped ones are 0
+// (the mask regenerated as in the dQ kernel).
+template <int D, bool DROP = false>
 __global__ __launch_bounds__(256, 2) void bwd_exact_d_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
     const u16* __restrict__ dO, const float* __restrict__ LSE, float* __restrict__ Dout, int H,
-    int N, float sl2, int causal, const int32_t* __restrict__ kv_len, int nqb, int total) {
+    int N, float sl2, int causal, const int32_t* __restrict__ kv_len, int nqb, int total,
+    DropParams dpar) {
   using C = ExactDCfg<D>;
   constexpr int BC = C::BC;
   __shared__ __attribute__((aligned(16))) u16 Ks[2][BC * C::KSTR];
@@ -180,14 +184,20 @@ __global__ __launch_bounds__(256, 2) void bwd_exact_d_kernel(
       // Key kb + 4g + c, c = 32mt + 8(e/4) + e%4, is hidden iff c > lim.
       const int lim = need_mask ? min(kv_lim - 1, causal ? q : kv_lim - 1) - (kb + 4 * g) : INT_MAX;
 #pragma unroll
-      for (int mt = 0; mt < BC / 32; ++mt)
+      for (int mt = 0; mt < BC / 32; ++mt) {
+        unsigned W[4];
+        if constexpr (DROP) drop_words_query_lane(dpar, bh, q, kb + 32 * mt, g, lane, W);
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int c = 32 * mt + 8 * (e >> 2) + (e & 3);
           float p = fast_exp2(s[mt][e] * sl2 - lse2);
           if (c > lim) p = 0.f;
-          part += p * dp[mt][e];
+          if constexpr (DROP)
+            part += drop_keep(W, e, dpar.thresh) ? p * dp[mt][e] * dpar.keep_scale : 0.f;
+          else
+            part += p * dp[mt][e];
         }
+      }
     }
     if (it + 1 < nt) store_tile(buf ^ 1);
     __syncthreads();
@@ -225,12 +235,16 @@ struct DkdvCfg {
 // double-buffered LDS tiles that serve as A operands both row-wise
 // (S = Q K^T, dP = dO V^T) and transposed (dV^T = dO^T P, dK^T = Q^T dS,
 // through ds_read_b64_tr_b16), with P and dS taken from registers.
-template <int D, bool PRECISE, bool DQ_ATOMIC>
+//
+// DROP: fused dropout regenerated from the generator state (fa_dropout.h):
+// dV takes the kept weights, dP of kept elements is scaled by the keep
+// factor and dropped ones contribute only the -P D term of dS.
+template <int D, bool PRECISE, bool DQ_ATOMIC, bool DROP = false>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
     const u16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dg,
     float* __restrict__ dQ, float* __restrict__ dK, float* __restrict__ dV, int H, int N, float scale,
-    float sl2, int causal, const int32_t* __restrict__ kv_len, int nkb, int total) {
+    float sl2, int causal, const int32_t* __restrict__ kv_len, int nkb, int total, DropParams dpar) {
   using C = DkdvCfg<D>;
   constexpr int BQ = C::BQ;
   constexpr int NSPLIT = PRECISE ? 2 : 1;
@@ -371,7 +385,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
             }
         }
 #pragma unroll
-        for (int qt = 0; qt < BQ / 32; ++qt)
+        for (int qt = 0; qt < BQ / 32; ++qt) {
+          unsigned W[4];
+          if constexpr (DROP) drop_words_key_lane(dpar, bh, key, q0 + 32 * qt, g, lane, W);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int ql = 32 * qt + 8 * i + 4 * g;
@@ -381,10 +397,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
             for (int j = 0; j < 4; ++j) {
               const int e = 4 * i + j;
               const float p = fast_exp2(sa[qt][e] * sl2 - l4[j]);
-              sa[qt][e] = p;
-              pa[qt][e] = p * (pa[qt][e] - d4[j]);
+              if constexpr (DROP) {
+                const bool keep = drop_keep(W, e, dpar.thresh);
+                sa[qt][e] = keep ? p : 0.f;
+                pa[qt][e] = p * ((keep ? pa[qt][e] * dpar.keep_scale : 0.f) - d4[j]);
+              } else {
+                sa[qt][e] = p;
+                pa[qt][e] = p * (pa[qt][e] - d4[j]);
+              }
             }
           }
+        }
         bf16x8 pb[BQ / 16], db[BQ / 16], pl[PRECISE ? BQ / 16 : 1], dl[PRECISE ? BQ / 16 : 1];
 #pragma unroll
         for (int c = 0; c < BQ / 16; ++c) {
@@ -487,7 +510,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           a[j] = dk[t][4 * i + j] * scale;
-          c[j] = dv[t][4 * i + j];
+          c[j] = DROP ? dv[t][4 * i + j] * dpar.keep_scale : dv[t][4 * i + j];
         }
         *reinterpret_cast<f32x4*>(dkrow + 32 * t + 8 * i + 4 * g) = a;
         *reinterpret_cast<f32x4*>(dvrow + 32 * t + 8 * i + 4 * g) = c;
@@ -520,12 +543,16 @@ struct DqCfg {
 // D_i = dO_i . O_i, from the dO rows it already holds and one read of O, and
 // stores it to Dg for the dK/dV kernel that runs after it (no separate
 // pre-pass). In precise mode it reads the exact D_i from Dg.
-template <int D, bool PRECISE>
+//
+// DROP: fused dropout regenerated from the generator state (fa_dropout.h);
+// dP of kept elements is scaled by the keep factor, dropped ones give
+// dS = -P D.
+template <int D, bool PRECISE, bool DROP = false>
 __global__ __launch_bounds__(256, PRECISE ? 1 : 2) void bwd_dq_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
     const u16* __restrict__ O, const u16* __restrict__ dO, const float* __restrict__ LSE,
     float* __restrict__ Dg, float* __restrict__ dQ, int H, int N, float scale, float sl2, int causal,
-    const int32_t* __restrict__ kv_len, int nqb, int total) {
+    const int32_t* __restrict__ kv_len, int nqb, int total, DropParams dpar) {
   using C = DqCfg<D>;
   constexpr int BC = C::BC, KSTR = C::KSTR, VSTR = C::VSTR;
   // Tiles arrive by direct-to-LDS loads. The two buffers of each tensor are
@@ -640,12 +667,18 @@ __global__ __launch_bounds__(256, PRECISE ? 1 : 2) void bwd_dq_kernel(
           }
       }
 #pragma unroll
-      for (int mt = 0; mt < BC / 32; ++mt)
+      for (int mt = 0; mt < BC / 32; ++mt) {
+        unsigned W[4];
+        if constexpr (DROP) drop_words_query_lane(dpar, bh, q, kb + 32 * mt, g, lane, W);
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const float p = fast_exp2(s[mt][e] * sl2 - lse2);
-          dp[mt][e] = p * (dp[mt][e] - Dq);
+          if constexpr (DROP)
+            dp[mt][e] = p * ((drop_keep(W, e, dpar.thresh) ? dp[mt][e] * dpar.keep_scale : 0.f) - Dq);
+          else
+            dp[mt][e] = p * (dp[mt][e] - Dq);
         }
+      }
       bf16x8 db[BC / 16], dl[PRECISE ? BC / 16 : 1];
 #pragma unroll
       for (int c = 0; c < BC / 16; ++c) {
@@ -688,24 +721,24 @@ __global__ __launch_bounds__(256, PRECISE ? 1 : 2) void bwd_dq_kernel(
   }
 }
 
-template <int D, bool PRECISE, bool DQ_ATOMIC>
+template <int D, bool PRECISE, bool DQ_ATOMIC, bool DROP = false>
 static void launch_dkdv(const u16* q, const u16* k, const u16* v, const u16* g, const float* LSE,
                         const float* Dws, float* dQ, float* dK, float* dV, const AttnShape& s, float sl2,
-                        hipStream_t stream) {
+                        hipStream_t stream, DropParams dp = {}) {
   const int nkb = (s.N + DkdvCfg<D>::BKV - 1) / DkdvCfg<D>::BKV;
   const int total = s.B * s.H * nkb;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, PRECISE, DQ_ATOMIC>), dim3(total), dim3(256), 0, stream, q, k, v, g,
-                     LSE, Dws, dQ, dK, dV, s.H, s.N, s.scale, sl2, s.causal, s.kv_len, nkb, total);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, PRECISE, DQ_ATOMIC, DROP>), dim3(total), dim3(256), 0, stream, q, k, v,
+                     g, LSE, Dws, dQ, dK, dV, s.H, s.N, s.scale, sl2, s.causal, s.kv_len, nkb, total, dp);
 }
 
-template <int D, bool PRECISE>
+template <int D, bool PRECISE, bool DROP = false>
 static void launch_dq(const u16* q, const u16* k, const u16* v, const u16* o, const u16* g,
                       const float* LSE, float* Dws, float* dQ, const AttnShape& s, float sl2,
-                      hipStream_t stream) {
+                      hipStream_t stream, DropParams dp = {}) {
   const int nqb = (s.N + DqCfg<D>::BR - 1) / DqCfg<D>::BR;
   const int total = s.B * s.H * nqb;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, PRECISE>), dim3(total), dim3(256), 0, stream, q, k, v, o, g, LSE,
-                     Dws, dQ, s.H, s.N, s.scale, sl2, s.causal, s.kv_len, nqb, total);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, PRECISE, DROP>), dim3(total), dim3(256), 0, stream, q, k, v, o, g, LSE,
+                     Dws, dQ, s.H, s.N, s.scale, sl2, s.causal, s.kv_len, nqb, total, dp);
 }
 
 // Entry points of the translation units: the key-outer kernel per head

@@ -35,7 +35,7 @@ static hipError_t launch_row_term(const BwdArgs& a, const AttnShape& s, bool pre
     const int nqb = (s.N + ExactDCfg<D>::BR - 1) / ExactDCfg<D>::BR;
     const int total = s.B * s.H * nqb;
     hipLaunchKernelGGL(bwd_exact_d_kernel<D>, dim3(total), dim3(256), 0, stream, q, k, v, g, a.LSE,
-                       a.Dws, s.H, s.N, s.scale * kLog2e, s.causal, s.kv_len, nqb, total);
+                       a.Dws, s.H, s.N, s.scale * kLog2e, s.causal, s.kv_len, nqb, total, DropParams{});
   } else {
     hipLaunchKernelGGL(bwd_dot_kernel<D>, dim3((unsigned)((rows * 16 + 255) / 256)), dim3(256), 0,
                        stream, o, g, a.Dws, (int)rows);

@@ -36,6 +36,7 @@
 #include <type_traits>
 
 #include "fa_common.h"
+#include "fa_dropout.h"
 #include "fa_launch.h"
 
 namespace fa {
@@ -86,11 +87,13 @@ using FwdCfg64Full = FwdCfg<64, 4, 2, false, 2>;
 // exceeds it by more than this, so unnormalised weights stay below 2^8.
 constexpr float kRescaleSlack = 8.f;
 
-template <int D, class C>
+// DROP: fused dropout on the normalised weights (see fa_dropout.h); the row
+// sums and the saved LSE are those of the undropped scores.
+template <int D, class C, bool DROP = false>
 __global__ __launch_bounds__(C::NT, C::OCC * 4 / C::NW) void fwd_bf16_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
     u16* __restrict__ O, float* __restrict__ LSE, int H, int N, float sl2, int causal,
-    const int32_t* __restrict__ kv_len, int nqb, int total) {
+    const int32_t* __restrict__ kv_len, int nqb, int total, DropParams dpar) {
   constexpr int BC = C::BC, NT = C::NT, QS = C::QS;
   constexpr bool DL = C::DL;
   // Register-staged tiles: two buffers per tensor, indexed at run time.
@@ -248,7 +251,7 @@ __global__ __launch_bounds__(C::NT, C::OCC * 4 / C::NW) void fwd_bf16_kernel(
   // `buf`: A = V^T rows d = 32t + r, k-slots = keys of chunk c in the order
   // of the score registers (16c + 8h + 4g + 0..3 for slots 4h..4h+3); each
   // V read serves all QS slabs.
-  auto exp_pv = [&](const u16* Vt, f32x16 (*sv)[BC / 32]) {
+  auto exp_pv = [&](const u16* Vt, f32x16 (*sv)[BC / 32], int kb) {
     bf16x8 pb[QS][BC / 16];
 #pragma unroll
     for (int s = 0; s < QS; ++s) {
@@ -263,6 +266,17 @@ __global__ __launch_bounds__(C::NT, C::OCC * 4 / C::NW) void fwd_bf16_kernel(
           rs += p;
         }
       l_run[s] += rs;
+      if constexpr (DROP) {
+        // Dropped weights leave the P V product; l keeps them.
+#pragma unroll
+        for (int mt = 0; mt < BC / 32; ++mt) {
+          unsigned W[4];
+          drop_words_query_lane(dpar, bh, wave_q_first + 32 * s + r, kb + 32 * mt, g, lane, W);
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            if (!drop_keep(W, e, dpar.thresh)) sv[s][mt][e] = 0.f;
+        }
+      }
 #pragma unroll
       for (int c = 0; c < BC / 16; ++c) pb[s][c] = pack_bf16x8(sv[s][c >> 1], 8 * (c & 1));
     }
@@ -302,7 +316,7 @@ __global__ __launch_bounds__(C::NT, C::OCC * 4 / C::NW) void fwd_bf16_kernel(
       if (it < nt_w) {
         mask_max(kb, cur);
         qk(P ? Kd0 : Kd1, nxt);
-        exp_pv(P ? Vd1 : Vd0, cur);
+        exp_pv(P ? Vd1 : Vd0, cur, kb);
       }
       // Each wave waits for its own loads before the barrier publishes them.
       wait_vmem_all();
@@ -344,7 +358,7 @@ __global__ __launch_bounds__(C::NT, C::OCC * 4 / C::NW) void fwd_bf16_kernel(
         // the result is dropped), independent of the softmax below.
         f32x16 s_next[QS][BC / 32];
         qk(Ks[(it + 1) & 1], s_next);
-        exp_pv(Vs[it & 1], s_cur);
+        exp_pv(Vs[it & 1], s_cur, kb);
 #pragma unroll
         for (int s = 0; s < QS; ++s)
 #pragma unroll
@@ -375,7 +389,7 @@ __global__ __launch_bounds__(C::NT, C::OCC * 4 / C::NW) void fwd_bf16_kernel(
       if (it < nt_w) {
         qk(Ks[it & 1], s_cur);
         mask_max(kb, s_cur);
-        exp_pv(Vs[it & 1], s_cur);
+        exp_pv(Vs[it & 1], s_cur, kb);
       }
       if (more) {
         store_k((it + 1) & 1);
@@ -389,7 +403,7 @@ __global__ __launch_bounds__(C::NT, C::OCC * 4 / C::NW) void fwd_bf16_kernel(
   for (int s = 0; s < QS; ++s) {
     const int q = wave_q_first + 32 * s + r;
     const float l_tot = pair_sum(l_run[s]);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float inv = l_tot > 0.f ? (DROP ? dpar.keep_scale : 1.f) / l_tot : 0.f;
     if (q < N) {
       u16* orow = O + head + (size_t)q * D;
 #pragma unroll
@@ -408,15 +422,15 @@ __global__ __launch_bounds__(C::NT, C::OCC * 4 / C::NW) void fwd_bf16_kernel(
   }
 }
 
-template <int D, class C>
+template <int D, class C, bool DROP = false>
 static hipError_t launch_fwd_d(const void* Q, const void* K, const void* V, void* O, float* LSE,
-                               const AttnShape& s, hipStream_t stream) {
+                               const AttnShape& s, hipStream_t stream, DropParams dp = {}) {
   const int nqb = (s.N + C::BR - 1) / C::BR;
   const int total = s.B * s.H * nqb;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, C>), dim3(total), dim3(C::NT), 0, stream,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, C, DROP>), dim3(total), dim3(C::NT), 0, stream,
                      static_cast<const u16*>(Q), static_cast<const u16*>(K),
                      static_cast<const u16*>(V), static_cast<u16*>(O), LSE, s.H, s.N,
-                     s.scale * kLog2e, s.causal, s.kv_len, nqb, total);
+                     s.scale * kLog2e, s.causal, s.kv_len, nqb, total, dp);
   return hipGetLastError();
 }
 

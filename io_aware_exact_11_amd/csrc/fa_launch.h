@@ -40,6 +40,26 @@ hipError_t launch_dkdv_atomic_bf16_d128(const BwdArgs& a, const AttnShape& s, bo
 hipError_t launch_dq_bf16_d64(const BwdArgs& a, const AttnShape& s, bool precise, hipStream_t stream);
 hipError_t launch_dq_bf16_d128(const BwdArgs& a, const AttnShape& s, bool precise, hipStream_t stream);
 
+// Fused dropout: Philox4x32-10 key words, the fourth counter word, the byte
+// threshold t = round(256 p) (kept iff byte >= t) and the keep factor
+// 256 / (256 - t).
+struct DropParams {
+  unsigned k0, k1;
+  unsigned offset;
+  unsigned thresh;
+  float keep_scale;
+};
+
+hipError_t launch_fwd_drop_bf16(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                                const AttnShape& s, const DropParams& dp, hipStream_t stream);
+hipError_t launch_bwd_drop_bf16(const void* Q, const void* K, const void* V, const void* O,
+                                const void* dO, const float* LSE, float* dQ, float* dK, float* dV,
+                                float* Dws, const AttnShape& s, const DropParams& dp, bool precise,
+                                hipStream_t stream);
+// The keep mask itself, [B, H, Nq, Nk] bytes (1 = kept).
+hipError_t launch_dropout_mask(uint8_t* mask, int B, int H, int Nq, int Nk, const DropParams& dp,
+                               hipStream_t stream);
+
 // Dws: fp32 [B,H,N] scratch for the per-row term D_i.
 hipError_t launch_bwd_bf16(const void* Q, const void* K, const void* V, const void* O,
                            const void* dO, const float* LSE, float* dQ, float* dK, float* dV,

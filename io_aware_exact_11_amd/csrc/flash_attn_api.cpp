@@ -97,6 +97,19 @@ size_t decode_ws_bytes(int B, int H, int Nq, int Nk, int d) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 
+// Dropout parameters: 0 <= p < 1 with round(256 p) < 256.
+int drop_params(float p, uint64_t seed, uint32_t offset, fa::DropParams* out) {
+  if (!isfinite(p) || p < 0.f || !(p < 1.f)) return FA_ERR_INVALID_ARG;
+  const double t = floor((double)p * 256.0 + 0.5);
+  if (t >= 256.0) return FA_ERR_INVALID_ARG;
+  out->k0 = (unsigned)(seed & 0xFFFFFFFFu);
+  out->k1 = (unsigned)(seed >> 32);
+  out->offset = offset;
+  out->thresh = (unsigned)t;
+  out->keep_scale = (float)(256.0 / (256.0 - t));
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -180,6 +193,44 @@ int flash_attn_decode_fwd(const void* Q, const void* K, const void* V, void* O, 
   const fa::DecodeShape s{B, H, Nq, Nk, d, scale, causal, kv_len};
   return hip_status(fa::launch_decode_bf16(Q, K, V, O, LSE, static_cast<float*>(workspace), s,
                                            static_cast<hipStream_t>(stream)));
+}
+
+int flash_attn_fwd_dropout(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
+                           int N, int d, float scale, int causal, const int32_t* kv_len, float p_drop,
+                           uint64_t seed, uint32_t offset, void* stream) {
+  fa::DropParams dp;
+  int st = drop_params(p_drop, seed, offset, &dp);
+  if (st != FA_OK) return st;
+  st = fwd_common(Q, K, V, O, LSE, B, H, N, d, scale, causal, 2);
+  if (st != FA_OK) return st;
+  const fa::AttnShape s{B, H, N, d, scale, causal, kv_len};
+  return hip_status(fa::launch_fwd_drop_bf16(Q, K, V, O, LSE, s, dp, static_cast<hipStream_t>(stream)));
+}
+
+int flash_attn_bwd_dropout(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                           const float* LSE, float* dQ, float* dK, float* dV, void* workspace,
+                           size_t workspace_bytes_, int B, int H, int N, int d, float scale, int causal,
+                           const int32_t* kv_len, float p_drop, uint64_t seed, uint32_t offset, unsigned flags,
+                           void* stream) {
+  fa::DropParams dp;
+  int st = drop_params(p_drop, seed, offset, &dp);
+  if (st != FA_OK) return st;
+  st = bwd_common(Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, workspace_bytes_, B, H, N, d, scale, causal, flags,
+                  FA_BWD_PRECISE, 2);
+  if (st != FA_OK) return st;
+  const fa::AttnShape s{B, H, N, d, scale, causal, kv_len};
+  return hip_status(fa::launch_bwd_drop_bf16(Q, K, V, O, dO, LSE, dQ, dK, dV, static_cast<float*>(workspace), s,
+                                             dp, (flags & FA_BWD_PRECISE) != 0, static_cast<hipStream_t>(stream)));
+}
+
+int flash_attn_dropout_mask(uint8_t* mask, int B, int H, int N_q, int N_k, float p_drop, uint64_t seed,
+                            uint32_t offset, void* stream) {
+  fa::DropParams dp;
+  int st = drop_params(p_drop, seed, offset, &dp);
+  if (st != FA_OK) return st;
+  if (!mask || B < 1 || H < 1 || N_q < 1 || N_k < 1) return FA_ERR_INVALID_ARG;
+  if ((int64_t)B * H > INT32_MAX) return FA_ERR_UNSUPPORTED;
+  return hip_status(fa::launch_dropout_mask(mask, B, H, N_q, N_k, dp, static_cast<hipStream_t>(stream)));
 }
 
 const char* flash_attn_status_string(int status) {

@@ -158,3 +158,47 @@ def _dec(lib, B=1, H=1, Nq=1, Nk=64, d=64, scale=0.125, causal=0, ws=None, ptrs=
 ])
 def test_decode_rejects(lib, kw, status):
     assert _dec(lib, **kw) == status
+
+
+def _fwd_drop(lib, p=0.1, B=1, d=64, ptrs=None):
+    N, span = 16, 1 * 1 * 16 * 128 * 2 + 4096
+    base = [FAKE + i * ((span + 4095) // 4096 * 4096) for i in range(5)]
+    if ptrs:
+        base = [ptrs.get(i, b) for i, b in enumerate(base)]
+    return lib.flash_attn_fwd_dropout(*[ctypes.c_void_p(x) if x is not None else None for x in base],
+                                      B, 1, N, d, 0.125, 0, None, p, 1234, 0, None)
+
+
+def _bwd_drop(lib, p=0.1, ws=None, d=64, ptrs=None, flags=0):
+    B, H, N = 1, 1, 16
+    step = (B * H * N * d * 4 + 4096 + 4095) // 4096 * 4096
+    base = [FAKE + i * step for i in range(10)]
+    if ptrs:
+        base = [ptrs.get(i, b) for i, b in enumerate(base)]
+    wsb = fa.flash_attn_bwd_workspace_bytes(B, H, N, d, 0) if ws is None else ws
+    return lib.flash_attn_bwd_dropout(*[ctypes.c_void_p(x) if x is not None else None for x in base], wsb,
+                                      B, H, N, d, 0.125, 0, None, p, 1234, 0, flags, None)
+
+
+@pytest.mark.parametrize("kw", [dict(p=-0.1), dict(p=1.0), dict(p=0.999), dict(p=math.nan), dict(p=math.inf),
+                                dict(B=0), dict(ptrs={0: None}), dict(ptrs={3: FAKE})])
+def test_fwd_dropout_rejects_invalid(lib, kw):
+    assert _fwd_drop(lib, **kw) == fa.binding.FA_ERR_INVALID_ARG
+
+
+def test_fwd_dropout_rejects_head_size(lib):
+    assert _fwd_drop(lib, d=96) == fa.binding.FA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw", [dict(p=-1e-3), dict(p=0.9990), dict(p=math.nan), dict(ws=16),
+                                dict(ptrs={9: None}), dict(ptrs={6: FAKE}), dict(flags=2), dict(flags=1 << 7)])
+def test_bwd_dropout_rejects_invalid(lib, kw):
+    assert _bwd_drop(lib, **kw) == fa.binding.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("args", [(None, 1, 1, 4, 4, 0.1), (FAKE, 0, 1, 4, 4, 0.1), (FAKE, 1, 1, 0, 4, 0.1),
+                                  (FAKE, 1, 1, 4, -2, 0.1), (FAKE, 1, 1, 4, 4, 1.0), (FAKE, 1, 1, 4, 4, -0.5)])
+def test_dropout_mask_rejects_invalid(lib, args):
+    m, B, H, nq, nk, p = args
+    assert lib.flash_attn_dropout_mask(ctypes.c_void_p(m) if m else None, B, H, nq, nk, p, 7, 0, None) == \
+        fa.binding.FA_ERR_INVALID_ARG
