@@ -14,7 +14,9 @@ The primary workload is the GPT-2-medium attention shape (B=64, H=16,
 N=1024, d=64, causal); the N=4096 and N=16384 head-dim-128 workloads are
 timed the same way and reported under "workloads", next to the decoding
 forward (one new query per head against a 32K-slot cache), which is
-memory-bound and reported as an HBM rate. Only one GPU is used.
+memory-bound and reported as an HBM rate, and the N=4096, d=128 workload
+again with fused dropout at p = 0.1 (same FLOP count; the generator work is
+not counted). Only one GPU is used.
 """
 from __future__ import annotations
 
@@ -31,6 +33,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 matrix-core peak (2.5 PFLOP/s class)
 PEAK_HBM_TBPS = 8.0        # MI355X HBM3E peak
 PRIMARY = "gpt2_medium"
+DROPOUT_SEED = 0x5EED  # generator key of the dropout workload
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -65,13 +68,13 @@ def kernel_source_digest():
 class Case:
     """Device-resident inputs and outputs of one workload."""
 
-    def __init__(self, name, causal, precise=False):
+    def __init__(self, name, causal, precise=False, dropout=None):
         import torch
         from io_aware_exact_11_amd import workloads as wl
         import io_aware_exact_11_amd as fa
         self.fa = fa
         self.w = wl.WORKLOADS[name]
-        self.name, self.causal, self.precise = name, causal, precise
+        self.name, self.causal, self.precise, self.dropout = name, causal, precise, dropout
         x = wl.workload_inputs(name)
         dev = lambda bits: torch.from_numpy(bits.view("int16")).view(torch.bfloat16).cuda()
         self.q, self.k, self.v, self.do = (dev(x[n + "_bits"]) for n in ("Q", "K", "V", "dO"))
@@ -90,10 +93,20 @@ class Case:
         self.pairs = pairs_per_batch(w, causal, self.kv_host)
 
     def fwd(self):
+        if self.dropout is not None:
+            self.fa.flash_attn_fwd_dropout(self.q, self.k, self.v, self.dropout, DROPOUT_SEED, 0, causal=self.causal,
+                                           scale=self.w.scale, kv_len=self.kv, out=self.o, lse=self.lse)
+            return
         self.fa.flash_attn_fwd(self.q, self.k, self.v, causal=self.causal, scale=self.w.scale,
                                kv_len=self.kv, out=self.o, lse=self.lse)
 
     def bwd(self):
+        if self.dropout is not None:
+            self.fa.flash_attn_bwd_dropout(self.q, self.k, self.v, self.o, self.do, self.lse, self.dropout,
+                                           DROPOUT_SEED, 0, causal=self.causal, scale=self.w.scale, kv_len=self.kv,
+                                           precise=self.precise, dq=self.dq, dk=self.dk, dv=self.dv,
+                                           workspace=self.ws)
+            return
         self.fa.flash_attn_bwd(self.q, self.k, self.v, self.o, self.do, self.lse, causal=self.causal,
                                scale=self.w.scale, kv_len=self.kv, precise=self.precise,
                                dq=self.dq, dk=self.dk, dv=self.dv, workspace=self.ws)
@@ -286,11 +299,13 @@ def main():
 
     if not args.no_extra:
         extra = []
-        for name, causal in (("n4096_d128", False), ("n4096_d128", True), ("long_16k", True)):
-            c = Case(name, causal)
+        for name, causal, drop in (("n4096_d128", False, None), ("n4096_d128", True, None), ("long_16k", True, None),
+                                   ("n4096_d128", False, 0.1)):
+            c = Case(name, causal, dropout=drop)
             wms, fms, bms = c.run(args.steps, args.warmup)
             cf, cb = c.flops()
-            extra.append({"workload": name, "causal": causal, "ms_per_step": round(wms, 4),
+            extra.append({"workload": name, "causal": causal, **({"dropout": drop} if drop else {}),
+                          "ms_per_step": round(wms, 4),
                           "fwd_tflops": round(cf / (fms * 1e-3) / 1e12, 2),
                           "fwd_frac": round(cf / (fms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                           "fwd_bwd_tflops": round((cf + cb) / (wms * 1e-3) / 1e12, 2),
