@@ -178,6 +178,21 @@ int flash_attn_bwd_dropout(const void* Q, const void* K, const void* V, const vo
 int flash_attn_dropout_mask(uint8_t* mask, int B, int H, int N_q, int N_k, float p_drop, uint64_t seed,
                             uint32_t offset, void* stream);
 
+/* Block-sparse forward ("FlashAttention and GPU Memory", chapters 10 and 12:
+ * the paper's approximate block-sparse variant, used for 64K-long inputs).
+ * block_mask is a DEVICE array of bytes, one per (query block, key block) of
+ * 128 x 128, row-major [nb][nb] with nb = ceil(N / 128) (query block index
+ * first); consecutive (b, h) masks are block_mask_head_stride bytes apart
+ * (0: every head uses the same mask). Key j is visible to query i iff
+ * block_mask[i/128][j/128] != 0, in addition to kv_len and causal; O and
+ * LSE are the exact softmax attention over the visible keys (O = 0,
+ * LSE = -inf for a row with none). Only key tiles of non-zero blocks are
+ * read from memory. N <= 65536 (larger: FA_ERR_UNSUPPORTED); NULL mask or a
+ * negative stride: FA_ERR_INVALID_ARG; other arguments as flash_attn_fwd. */
+int flash_attn_fwd_block_sparse(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
+                                int N, int d, float scale, int causal, const int32_t* kv_len,
+                                const uint8_t* block_mask, int64_t block_mask_head_stride, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* flash_attn_status_string(int status);
 

@@ -23,7 +23,7 @@ FA_BWD_DQ_ATOMIC = 2
 EXPORTED = ("flash_attn_fwd", "flash_attn_bwd", "flash_attn_bwd_workspace_bytes",
             "flash_attn_fwd_f32", "flash_attn_bwd_f32", "flash_attn_decode_fwd",
             "flash_attn_decode_workspace_bytes", "flash_attn_fwd_dropout", "flash_attn_bwd_dropout",
-            "flash_attn_dropout_mask", "flash_attn_status_string")
+            "flash_attn_dropout_mask", "flash_attn_fwd_block_sparse", "flash_attn_status_string")
 
 
 class FlashAttnError(RuntimeError):
@@ -66,6 +66,8 @@ def load_library():
     lib.flash_attn_bwd_dropout.restype = ctypes.c_int
     lib.flash_attn_dropout_mask.argtypes = [p, i, i, i, i, f, u64, u, p]
     lib.flash_attn_dropout_mask.restype = ctypes.c_int
+    lib.flash_attn_fwd_block_sparse.argtypes = fwd_args[:-1] + [p, ctypes.c_int64, p]
+    lib.flash_attn_fwd_block_sparse.restype = ctypes.c_int
     lib.flash_attn_status_string.argtypes = [i]
     lib.flash_attn_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -248,3 +250,22 @@ def flash_attn_dropout_mask(B, H, N_q, N_k, p_drop, seed, offset=0, out=None, de
     if st != FA_OK:
         raise FlashAttnError(st, "flash_attn_dropout_mask")
     return out
+
+
+def flash_attn_fwd_block_sparse(q, k, v, block_mask, causal=False, scale=None, kv_len=None, out=None, lse=None):
+    """bf16 block-sparse forward. block_mask: uint8 (or bool) device tensor [nb, nb] shared by every head, or
+    [B, H, nb, nb], nb = ceil(N / 128). Returns (O bf16, LSE fp32)."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    nb = (N + 127) // 128
+    if block_mask.dtype == torch.bool:
+        block_mask = block_mask.to(torch.uint8)
+    if tuple(block_mask.shape) == (nb, nb):
+        stride = 0
+    else:
+        _check("block_mask", block_mask, torch.uint8, (B, H, nb, nb))
+        stride = nb * nb
+    _check("block_mask", block_mask, torch.uint8, block_mask.shape)
+    return _fwd("flash_attn_fwd_block_sparse", torch.bfloat16, q, k, v, causal, scale, kv_len, out, lse,
+                (_ptr(block_mask), stride))

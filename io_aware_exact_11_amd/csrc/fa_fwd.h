@@ -87,13 +87,24 @@ using FwdCfg64Full = FwdCfg<64, 4, 2, false, 2>;
 // exceeds it by more than this, so unnormalised weights stay below 2^8.
 constexpr float kRescaleSlack = 8.f;
 
+// Block-sparse attention: blocks of kSparseBlock queries by kSparseBlock keys,
+// at most kSparseMaxTiles key tiles (N <= 65536) per row of blocks.
+constexpr int kSparseBlock = 128;
+constexpr int kSparseMaxTiles = 1024;
+
 // DROP: fused dropout on the normalised weights (see fa_dropout.h); the row
 // sums and the saved LSE are those of the undropped scores.
-template <int D, class C, bool DROP = false>
+// SPARSE: block-sparse attention ("FlashAttention and GPU Memory", chapters
+// 10 and 12 name the approximate block-sparse variant). bmask holds one byte
+// per (query block, key block) of 128 x 128, row-major, bmask_stride bytes
+// apart for consecutive (b, h); only key tiles whose block is on are loaded
+// and computed, on top of the causal and padding masks.
+template <int D, class C, bool DROP = false, bool SPARSE = false>
 __global__ __launch_bounds__(C::NT, C::OCC * 4 / C::NW) void fwd_bf16_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
     u16* __restrict__ O, float* __restrict__ LSE, int H, int N, float sl2, int causal,
-    const int32_t* __restrict__ kv_len, int nqb, int total, DropParams dpar) {
+    const int32_t* __restrict__ kv_len, int nqb, int total, DropParams dpar,
+    const uint8_t* __restrict__ bmask, long long bmask_stride) {
   constexpr int BC = C::BC, NT = C::NT, QS = C::QS;
   constexpr bool DL = C::DL;
   // Register-staged tiles: two buffers per tensor, indexed at run time.
@@ -129,7 +140,35 @@ __global__ __launch_bounds__(C::NT, C::OCC * 4 / C::NW) void fwd_bf16_kernel(
   }
   int kv_end = kv_lim;
   if (causal) kv_end = min(kv_end, q0 + C::BR);
-  const int nt = (kv_end + BC - 1) / BC;
+  // Block-sparse: the ascending list of key tiles (64 keys, half a block)
+  // whose block is on for this workgroup's 128 query rows, built by wave 0
+  // with a ballot prefix count; the loop runs over the list and its tile t
+  // starts at key tkb(t).
+  static_assert(!SPARSE || (C::BR == kSparseBlock && BC * 2 == kSparseBlock), "sparse tiles");
+  __shared__ unsigned short tlist[SPARSE ? kSparseMaxTiles : 1];
+  __shared__ int tlist_n;
+  auto sparse_list = [&](int nt_all) {
+    if (tid < 64) {
+      const uint8_t* brow = bmask + (size_t)bh * bmask_stride + (size_t)qb * ((N + kSparseBlock - 1) / kSparseBlock);
+      int cnt = 0;
+      for (int t0 = 0; t0 < nt_all; t0 += 64) {
+        const int t = t0 + tid;
+        const bool on = t < nt_all && brow[t >> 1] != 0;
+        const unsigned long long bal = __builtin_amdgcn_ballot_w64(on);
+        const int pos = cnt + (int)__builtin_amdgcn_mbcnt_hi((unsigned)(bal >> 32),
+                                                             __builtin_amdgcn_mbcnt_lo((unsigned)bal, 0u));
+        if (on) tlist[pos] = (unsigned short)t;
+        cnt += __popcll(bal);
+      }
+      if (tid == 0) tlist_n = cnt;
+    }
+    __syncthreads();
+    return tlist_n;
+  };
+  const int nt = SPARSE ? sparse_list((kv_end + BC - 1) / BC) : (kv_end + BC - 1) / BC;
+  // Start of loop tile t + k given the start kb of tile t (the dense loop
+  // keeps its own arithmetic).
+  auto tnext = [&](int t, int kb, int k) { return SPARSE ? (int)tlist[t + k] * BC : kb + k * BC; };
 
   // Slab s of wave w holds query rows q0 + 32*(QS*w + s) + 0..31; this lane
   // owns row r of each slab.
@@ -206,7 +245,17 @@ __global__ __launch_bounds__(C::NT, C::OCC * 4 / C::NW) void fwd_bf16_kernel(
   // 4g + (lane % 16) / 4, column part 16 * ((lane / 16) % 2) + 4 * (lane % 4).
   const int v_tr_off = (4 * g + ((lane & 15) >> 2)) * C::VSTR + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   // Causal waves compute only the tiles that reach their rows (a prefix).
-  const int nt_w = causal ? min(nt, wave_q_last / BC + 1) : nt;
+  // Causal block-sparse: the listed tiles that reach this wave's rows (a
+  // prefix of the ascending list).
+  auto sparse_prefix = [&]() {
+    int c = 0;
+    for (int i0 = 0; i0 < nt; i0 += 64) {
+      const bool in = i0 + lane < nt && (int)tlist[i0 + lane] <= wave_q_last / BC;
+      c += __popcll(__builtin_amdgcn_ballot_w64(in));
+    }
+    return c;
+  };
+  const int nt_w = causal ? (SPARSE ? sparse_prefix() : min(nt, wave_q_last / BC + 1)) : nt;
 
   // Mask, running maximum and lazy rescale of one tile's scores.
   auto mask_max = [&](int kb, f32x16 (*sv)[BC / 32]) {
@@ -299,10 +348,10 @@ __global__ __launch_bounds__(C::NT, C::OCC * 4 / C::NW) void fwd_bf16_kernel(
     // K_j left, V_{j+1} into the one V_{j-1} left. Two tiles per trip so
     // that the buffer names are compile-time constants.
     if (nt > 0) {
-      tile_to_lds_padded<D, C::KSTR, BC, C::NW>(rK, 0, Kd0, w, lane);
-      tile_to_lds_padded<D, C::VSTR, BC, C::NW>(rV, 0, Vd0, w, lane);
+      tile_to_lds_padded<D, C::KSTR, BC, C::NW>(rK, tnext(0, 0, 0), Kd0, w, lane);
+      tile_to_lds_padded<D, C::VSTR, BC, C::NW>(rV, tnext(0, 0, 0), Vd0, w, lane);
     }
-    if (nt > 1) tile_to_lds_padded<D, C::KSTR, BC, C::NW>(rK, BC, Kd1, w, lane);
+    if (nt > 1) tile_to_lds_padded<D, C::KSTR, BC, C::NW>(rK, tnext(0, 0, 1), Kd1, w, lane);
     wait_vmem_all();
     __syncthreads();
     if (nt_w > 0) qk(Kd0, s_cur);
@@ -310,9 +359,9 @@ __global__ __launch_bounds__(C::NT, C::OCC * 4 / C::NW) void fwd_bf16_kernel(
     f32x16 s_alt[QS][BC / 32];
     auto tile = [&](auto odd, int it, f32x16 (*cur)[BC / 32], f32x16 (*nxt)[BC / 32]) {
       constexpr bool P = decltype(odd)::value;
-      const int kb = it * BC;
-      if (it + 2 < nt) tile_to_lds_padded<D, C::KSTR, BC, C::NW>(rK, kb + 2 * BC, P ? Kd1 : Kd0, w, lane);
-      if (it + 1 < nt) tile_to_lds_padded<D, C::VSTR, BC, C::NW>(rV, kb + BC, P ? Vd0 : Vd1, w, lane);
+      const int kb = tnext(it, it * BC, 0);
+      if (it + 2 < nt) tile_to_lds_padded<D, C::KSTR, BC, C::NW>(rK, tnext(it, kb, 2), P ? Kd1 : Kd0, w, lane);
+      if (it + 1 < nt) tile_to_lds_padded<D, C::VSTR, BC, C::NW>(rV, tnext(it, kb, 1), P ? Vd0 : Vd1, w, lane);
       if (it < nt_w) {
         mask_max(kb, cur);
         qk(P ? Kd0 : Kd1, nxt);
@@ -331,13 +380,13 @@ __global__ __launch_bounds__(C::NT, C::OCC * 4 / C::NW) void fwd_bf16_kernel(
     // ALUs the wave already issues tile j+1's S^T products. K_j sits in
     // Ks[j % 2], V_j in Vs[j % 2]; one barrier per tile.
     if (nt > 0) {
-      load_k(0);
-      load_v(0);
+      load_k(tnext(0, 0, 0));
+      load_v(tnext(0, 0, 0));
       store_k(0);
       store_v(0);
     }
     if (nt > 1) {
-      load_k(BC);
+      load_k(tnext(0, 0, 1));
       store_k(1);
     }
     __syncthreads();
@@ -348,10 +397,10 @@ __global__ __launch_bounds__(C::NT, C::OCC * 4 / C::NW) void fwd_bf16_kernel(
     wait_vmem_all();
 
     for (int it = 0; it < nt; ++it) {
-      const int kb = it * BC;
+      const int kb = tnext(it, it * BC, 0);
       const bool more_k = it + 2 < nt, more_v = it + 1 < nt;
-      if (more_k) load_k(kb + 2 * BC);
-      if (more_v) load_v(kb + BC);
+      if (more_k) load_k(tnext(it, kb, 2));
+      if (more_v) load_v(tnext(it, kb, 1));
       if (it < nt_w) {
         mask_max(kb, s_cur);
         // Next tile's scores (on the last tile this reads a stale buffer and
@@ -372,19 +421,19 @@ __global__ __launch_bounds__(C::NT, C::OCC * 4 / C::NW) void fwd_bf16_kernel(
     // K_j and V_j both sit in buffer j % 2; tile j+1 is loaded into
     // registers while tile j is computed and stored after it.
     if (nt > 0) {
-      load_k(0);
-      load_v(0);
+      load_k(tnext(0, 0, 0));
+      load_v(tnext(0, 0, 0));
       store_k(0);
       store_v(0);
     }
     __syncthreads();
     wait_vmem_all();
     for (int it = 0; it < nt; ++it) {
-      const int kb = it * BC;
+      const int kb = tnext(it, it * BC, 0);
       const bool more = it + 1 < nt;
       if (more) {
-        load_k(kb + BC);
-        load_v(kb + BC);
+        load_k(tnext(it, kb, 1));
+        load_v(tnext(it, kb, 1));
       }
       if (it < nt_w) {
         qk(Ks[it & 1], s_cur);
@@ -422,15 +471,16 @@ __global__ __launch_bounds__(C::NT, C::OCC * 4 / C::NW) void fwd_bf16_kernel(
   }
 }
 
-template <int D, class C, bool DROP = false>
+template <int D, class C, bool DROP = false, bool SPARSE = false>
 static hipError_t launch_fwd_d(const void* Q, const void* K, const void* V, void* O, float* LSE,
-                               const AttnShape& s, hipStream_t stream, DropParams dp = {}) {
+                               const AttnShape& s, hipStream_t stream, DropParams dp = {},
+                               const uint8_t* bmask = nullptr, long long bmask_stride = 0) {
   const int nqb = (s.N + C::BR - 1) / C::BR;
   const int total = s.B * s.H * nqb;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, C, DROP>), dim3(total), dim3(C::NT), 0, stream,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, C, DROP, SPARSE>), dim3(total), dim3(C::NT), 0, stream,
                      static_cast<const u16*>(Q), static_cast<const u16*>(K),
                      static_cast<const u16*>(V), static_cast<u16*>(O), LSE, s.H, s.N,
-                     s.scale * kLog2e, s.causal, s.kv_len, nqb, total, dp);
+                     s.scale * kLog2e, s.causal, s.kv_len, nqb, total, dp, bmask, bmask_stride);
   return hipGetLastError();
 }
 

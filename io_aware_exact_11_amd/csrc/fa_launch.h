@@ -60,6 +60,12 @@ hipError_t launch_bwd_drop_bf16(const void* Q, const void* K, const void* V, con
 hipError_t launch_dropout_mask(uint8_t* mask, int B, int H, int Nq, int Nk, const DropParams& dp,
                                hipStream_t stream);
 
+// Block-sparse forward: bmask bytes [nb][nb] per (b, h), nb = ceil(N / 128),
+// bmask_stride bytes between consecutive (b, h) (0: one mask for all heads).
+hipError_t launch_fwd_sparse_bf16(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                                  const AttnShape& s, const uint8_t* bmask, long long bmask_stride,
+                                  hipStream_t stream);
+
 // Dws: fp32 [B,H,N] scratch for the per-row term D_i.
 hipError_t launch_bwd_bf16(const void* Q, const void* K, const void* V, const void* O,
                            const void* dO, const float* LSE, float* dQ, float* dK, float* dV,

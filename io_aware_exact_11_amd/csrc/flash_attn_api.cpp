@@ -223,6 +223,18 @@ int flash_attn_bwd_dropout(const void* Q, const void* K, const void* V, const vo
                                              dp, (flags & FA_BWD_PRECISE) != 0, static_cast<hipStream_t>(stream)));
 }
 
+int flash_attn_fwd_block_sparse(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
+                                int N, int d, float scale, int causal, const int32_t* kv_len,
+                                const uint8_t* block_mask, int64_t block_mask_head_stride, void* stream) {
+  int st = fwd_common(Q, K, V, O, LSE, B, H, N, d, scale, causal, 2);
+  if (st != FA_OK) return st;
+  if (!block_mask || block_mask_head_stride < 0) return FA_ERR_INVALID_ARG;
+  if (N > 65536) return FA_ERR_UNSUPPORTED;
+  const fa::AttnShape s{B, H, N, d, scale, causal, kv_len};
+  return hip_status(fa::launch_fwd_sparse_bf16(Q, K, V, O, LSE, s, block_mask, (long long)block_mask_head_stride,
+                                               static_cast<hipStream_t>(stream)));
+}
+
 int flash_attn_dropout_mask(uint8_t* mask, int B, int H, int N_q, int N_k, float p_drop, uint64_t seed,
                             uint32_t offset, void* stream) {
   fa::DropParams dp;

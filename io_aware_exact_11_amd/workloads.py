@@ -121,6 +121,22 @@ DECODE_WORKLOADS = {
 }
 
 
+# Block-sparse workload: the 64K sequence length the pages' block-sparse
+# variant was used for (Path-256), with a synthetic pattern: every query block
+# of 128 rows sees its own key block, the two on each side, and key block 0
+# (a band plus one global column), about 1.2% of the blocks at N = 65536.
+BLOCK_SPARSE_WORKLOADS = {
+    "sparse_64k": dict(B=1, H=16, N=65536, d=128, band=2, causal=False, seed=7),
+}
+
+
+def block_sparse_pattern(N: int, band: int, block: int = 128) -> np.ndarray:
+    """uint8 [nb, nb] block mask: |qb - kb| <= band, plus key block 0."""
+    nb = (N + block - 1) // block
+    qb, kb = np.meshgrid(np.arange(nb), np.arange(nb), indexing="ij")
+    return ((np.abs(qb - kb) <= band) | (kb == 0)).astype(np.uint8)
+
+
 def make_decode_inputs(B: int, H: int, Nq: int, Nk: int, d: int, seed: int, ragged: bool = False) -> dict:
     """Q [B,H,Nq,d], K and V [B,H,Nk,d] (bf16 values as float32 plus "_bits"),
     and "kv_len" (int32 [B], ragged) or None."""

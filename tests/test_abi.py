@@ -202,3 +202,25 @@ def test_dropout_mask_rejects_invalid(lib, args):
     m, B, H, nq, nk, p = args
     assert lib.flash_attn_dropout_mask(ctypes.c_void_p(m) if m else None, B, H, nq, nk, p, 7, 0, None) == \
         fa.binding.FA_ERR_INVALID_ARG
+
+
+def _fwd_sparse(lib, N=256, d=64, mask=FAKE + (1 << 24), stride=0, ptrs=None):
+    span = 1 * 1 * N * 128 * 2 + 4096
+    base = [FAKE + i * ((span + 4095) // 4096 * 4096) for i in range(5)]
+    if ptrs:
+        base = [ptrs.get(i, b) for i, b in enumerate(base)]
+    return lib.flash_attn_fwd_block_sparse(*[ctypes.c_void_p(x) if x is not None else None for x in base],
+                                           1, 1, N, d, 0.125, 0, None,
+                                           ctypes.c_void_p(mask) if mask else None, stride, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(mask=None), fa.binding.FA_ERR_INVALID_ARG),
+    (dict(stride=-1), fa.binding.FA_ERR_INVALID_ARG),
+    (dict(N=65537), fa.binding.FA_ERR_UNSUPPORTED),
+    (dict(d=96), fa.binding.FA_ERR_UNSUPPORTED),
+    (dict(ptrs={1: None}), fa.binding.FA_ERR_INVALID_ARG),
+    (dict(ptrs={3: FAKE}), fa.binding.FA_ERR_INVALID_ARG),
+])
+def test_block_sparse_rejects(lib, kw, status):
+    assert _fwd_sparse(lib, **kw) == status
