@@ -16,7 +16,8 @@ timed the same way and reported under "workloads", next to the decoding
 forward (one new query per head against a 32K-slot cache), which is
 memory-bound and reported as an HBM rate, and the N=4096, d=128 workload
 again with fused dropout at p = 0.1 (same FLOP count; the generator work is
-not counted). Only one GPU is used.
+not counted), and the block-sparse forward on a 64K-long sequence (FLOPs
+over the visible pairs of its block mask). Only one GPU is used.
 """
 from __future__ import annotations
 
@@ -201,6 +202,44 @@ def decode_case(steps, warmup):
             "hbm_frac": round(gbps / (PEAK_HBM_TBPS * 1e3), 4), "algorithmic_bytes": nbytes}
 
 
+def block_sparse_case(steps, warmup):
+    """The block-sparse forward on the 64K-long workload (band of two blocks
+    each side plus key block 0): time per call from events on the stream,
+    TFLOP/s over the visible (query, key) pairs, and the fraction of the
+    dense pairs that is computed."""
+    import torch
+    import io_aware_exact_11_amd as fa
+    from io_aware_exact_11_amd import workloads as wl
+    name = "sparse_64k"
+    c = wl.BLOCK_SPARSE_WORKLOADS[name]
+    B, H, N, d = c["B"], c["H"], c["N"], c["d"]
+    x = wl.make_inputs(B, H, N, d, c["seed"])
+    dev = lambda bits: torch.from_numpy(bits.view("int16")).view(torch.bfloat16).cuda()
+    q, k, v = (dev(x[n + "_bits"]) for n in ("Q", "K", "V"))
+    del x
+    bm_host = wl.block_sparse_pattern(N, c["band"])
+    bm = torch.from_numpy(bm_host).cuda()
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    scale = float(d) ** -0.5
+    for _ in range(warmup):
+        fa.flash_attn_fwd_block_sparse(q, k, v, bm, causal=c["causal"], scale=scale, out=o, lse=lse)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        fa.flash_attn_fwd_block_sparse(q, k, v, bm, causal=c["causal"], scale=scale, out=o, lse=lse)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    # N is a multiple of 128 and the workload is non-causal: every on block is 128 x 128 visible pairs.
+    pairs = int(bm_host.sum()) * 128 * 128 * B * H
+    tflops = 4 * d * pairs / (ms * 1e-3) / 1e12
+    return {"workload": name, "kind": "block-sparse forward", "B": B, "H": H, "N": N, "d": d,
+            "block_density": round(float(bm_host.mean()), 5), "ms_per_call": round(ms, 4),
+            "fwd_tflops": round(tflops, 2), "fwd_frac": round(tflops / PEAK_BF16_TFLOPS, 4)}
+
+
 def memory_sweep():
     """Peak device memory of one fwd+bwd step (inputs, outputs, workspace) at
     B=2, H=16, d=128, causal, for growing N: grows linearly in N."""
@@ -313,6 +352,8 @@ def main():
             del c
             torch.cuda.empty_cache()
         extra.append(decode_case(args.steps, args.warmup))
+        extra.append(block_sparse_case(args.steps, args.warmup))
+        torch.cuda.empty_cache()
         result["workloads"] = extra
         result["memory_sweep_B2_H16_d128_causal"] = memory_sweep()
 
