@@ -121,6 +121,38 @@ DECODE_WORKLOADS = {
 }
 
 
+# 8-bit forward workload: the N=4096, d=128 shape with Q, K, V quantised to
+# FP8 E4M3, one scale per tensor (largest magnitude mapped to 448).
+FP8_WORKLOADS = {
+    "n4096_d128_fp8": dict(B=16, H=16, N=4096, d=128, causal=False, qkv_scale=0.5, seed=8),
+}
+
+
+def make_fp8_inputs(B: int, H: int, N: int, d: int, seed: int, qkv_scale: float = 1.0,
+                    outlier_cols: int = 0) -> dict:
+    """Q, K, V [B, H, N, d] drawn like make_inputs (fp32, times qkv_scale; with outlier_cols > 0 that many
+    feature columns of Q and K are multiplied by 8), then quantised to FP8 E4M3 per tensor with torch's
+    float8_e4m3fn conversion after dividing by amax / 448. Returns the codes "Q8", "K8" [B, H, N, d] and
+    "Vt8" [B, H, d, N] (V transposed), the fp32 dequantisation factors "dq", "dk", "dv", and the unquantised
+    float32 tensors "Q", "K", "V"."""
+    import torch
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = {}
+    for name in ("Q", "K", "V"):
+        out[name] = rng.standard_normal(size=(B, H, N, d), dtype=np.float32) * np.float32(qkv_scale)
+    if outlier_cols:
+        cols = rng.choice(d, size=outlier_cols, replace=False)
+        out["Q"][..., cols] *= np.float32(8.0)
+        out["K"][..., cols] *= np.float32(8.0)
+    for name, key in (("Q", "dq"), ("K", "dk"), ("V", "dv")):
+        f = np.float32(np.abs(out[name]).max() / 448.0)
+        codes = torch.from_numpy(out[name] / f).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        out[key] = float(f)
+        out[name + "8"] = codes
+    out["Vt8"] = np.ascontiguousarray(out.pop("V8").transpose(0, 1, 3, 2))
+    return out
+
+
 # Block-sparse workload: the 64K sequence length the pages' block-sparse
 # variant was used for (Path-256), with a synthetic pattern: every query block
 # of 128 rows sees its own key block, the two on each side, and key block 0

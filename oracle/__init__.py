@@ -8,4 +8,4 @@ from .attention import (  # noqa: F401
     forward_rows, online_softmax, blockwise_attention_row, decode_visible_mask,
     decode_head_forward, decode_forward,
 )
-from . import block_sparse, dropout  # noqa: F401
+from . import block_sparse, dropout, fp8  # noqa: F401
