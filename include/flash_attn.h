@@ -193,6 +193,20 @@ int flash_attn_fwd_block_sparse(const void* Q, const void* K, const void* V, voi
                                 int N, int d, float scale, int causal, const int32_t* kv_len,
                                 const uint8_t* block_mask, int64_t block_mask_head_stride, void* stream);
 
+/* 8-bit floating-point forward ("FlashAttention — why it mattered" and
+ * "FlashAttention and GPU Memory", chapter 11: the FlashAttention-3 8-bit
+ * mode, the method's one source of error beyond rounding order). Q8 and K8
+ * are OCP FP8 E4M3 codes (one byte each, [B, H, N, d]); Vt8 holds V
+ * transposed, [B, H, d, N]; every value must be finite. The inputs stand for
+ * Q = descale_q * Q8, K = descale_k * K8, V = descale_v * Vt8^T (fp32 factors,
+ * finite and > 0). O (bf16, [B, H, N, d]) and LSE (fp32, natural log) are
+ * the attention of those values: scores and softmax in fp32, the softmax
+ * weights rounded to E4M3 for the P V product. Other arguments and
+ * conventions as flash_attn_fwd. */
+int flash_attn_fwd_fp8(const void* Q8, const void* K8, const void* Vt8, void* O, float* LSE, int B, int H, int N,
+                       int d, float scale, int causal, const int32_t* kv_len, float descale_q, float descale_k,
+                       float descale_v, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* flash_attn_status_string(int status);
 

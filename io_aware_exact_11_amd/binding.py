@@ -23,7 +23,8 @@ FA_BWD_DQ_ATOMIC = 2
 EXPORTED = ("flash_attn_fwd", "flash_attn_bwd", "flash_attn_bwd_workspace_bytes",
             "flash_attn_fwd_f32", "flash_attn_bwd_f32", "flash_attn_decode_fwd",
             "flash_attn_decode_workspace_bytes", "flash_attn_fwd_dropout", "flash_attn_bwd_dropout",
-            "flash_attn_dropout_mask", "flash_attn_fwd_block_sparse", "flash_attn_status_string")
+            "flash_attn_dropout_mask", "flash_attn_fwd_block_sparse", "flash_attn_fwd_fp8",
+            "flash_attn_status_string")
 
 
 class FlashAttnError(RuntimeError):
@@ -68,6 +69,8 @@ def load_library():
     lib.flash_attn_dropout_mask.restype = ctypes.c_int
     lib.flash_attn_fwd_block_sparse.argtypes = fwd_args[:-1] + [p, ctypes.c_int64, p]
     lib.flash_attn_fwd_block_sparse.restype = ctypes.c_int
+    lib.flash_attn_fwd_fp8.argtypes = fwd_args[:-1] + [f, f, f, p]
+    lib.flash_attn_fwd_fp8.restype = ctypes.c_int
     lib.flash_attn_status_string.argtypes = [i]
     lib.flash_attn_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -269,3 +272,27 @@ def flash_attn_fwd_block_sparse(q, k, v, block_mask, causal=False, scale=None, k
     _check("block_mask", block_mask, torch.uint8, block_mask.shape)
     return _fwd("flash_attn_fwd_block_sparse", torch.bfloat16, q, k, v, causal, scale, kv_len, out, lse,
                 (_ptr(block_mask), stride))
+
+
+def flash_attn_fwd_fp8(q8, k8, vt8, descale_q, descale_k, descale_v, causal=False, scale=None, kv_len=None,
+                       out=None, lse=None):
+    """8-bit forward: q8, k8 uint8 E4M3 codes [B, H, N, d]; vt8 [B, H, d, N] (V transposed); fp32
+    dequantisation factors. Returns (O bf16 [B, H, N, d], LSE fp32 [B, H, N])."""
+    lib = load_library()
+    _check("q8", q8, torch.uint8, q8.shape)
+    if q8.dim() != 4:
+        raise ValueError("q8 must be [B, H, N, d]")
+    B, H, N, d = q8.shape
+    _check("k8", k8, torch.uint8, (B, H, N, d))
+    _check("vt8", vt8, torch.uint8, (B, H, d, N))
+    out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device) if out is None else out
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device) if lse is None else lse
+    _check("out", out, torch.bfloat16, (B, H, N, d))
+    _check("lse", lse, torch.float32, (B, H, N))
+    kv_len = _kv(kv_len, B, q8.device)
+    st = lib.flash_attn_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(vt8), _ptr(out), _ptr(lse), B, H, N, d, _scale(scale, d),
+                                int(bool(causal)), _ptr(kv_len), float(descale_q), float(descale_k),
+                                float(descale_v), _stream())
+    if st != FA_OK:
+        raise FlashAttnError(st, "flash_attn_fwd_fp8")
+    return out, lse

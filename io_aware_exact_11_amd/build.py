@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libflashattn.so")
 SOURCES = ["fa_fwd.hip", "fa_fwd_d64.hip", "fa_fwd_d128.hip", "fa_bwd.hip", "fa_bwd_dkdv_d64.hip",
-           "fa_bwd_dkdv_d128.hip", "fa_bwd_dkdv_atomic.hip", "fa_bwd_dq_d64.hip", "fa_bwd_dq_d128.hip", "fa_decode.hip", "fa_drop_fwd.hip", "fa_drop_bwd.hip", "fa_sparse_fwd.hip", "fa_f32.hip",
+           "fa_bwd_dkdv_d128.hip", "fa_bwd_dkdv_atomic.hip", "fa_bwd_dq_d64.hip", "fa_bwd_dq_d128.hip", "fa_decode.hip", "fa_drop_fwd.hip", "fa_drop_bwd.hip", "fa_sparse_fwd.hip", "fa_fwd_fp8.hip", "fa_f32.hip",
            "flash_attn_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 VALU forms are switched off for all device code. Matrix-core

@@ -66,6 +66,11 @@ hipError_t launch_fwd_sparse_bf16(const void* Q, const void* K, const void* V, v
                                   const AttnShape& s, const uint8_t* bmask, long long bmask_stride,
                                   hipStream_t stream);
 
+// 8-bit forward: Q8, K8 E4M3 [B,H,N,d], Vt8 E4M3 [B,H,d,N], fp32 dequantisation
+// factors; O bf16, LSE fp32.
+hipError_t launch_fwd_fp8(const void* Q8, const void* K8, const void* Vt8, void* O, float* LSE, const AttnShape& s,
+                          float dq, float dk, float dv, hipStream_t stream);
+
 // Dws: fp32 [B,H,N] scratch for the per-row term D_i.
 hipError_t launch_bwd_bf16(const void* Q, const void* K, const void* V, const void* O,
                            const void* dO, const float* LSE, float* dQ, float* dK, float* dV,

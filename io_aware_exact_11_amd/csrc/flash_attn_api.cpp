@@ -235,6 +235,28 @@ int flash_attn_fwd_block_sparse(const void* Q, const void* K, const void* V, voi
                                                static_cast<hipStream_t>(stream)));
 }
 
+int flash_attn_fwd_fp8(const void* Q8, const void* K8, const void* Vt8, void* O, float* LSE, int B, int H, int N,
+                       int d, float scale, int causal, const int32_t* kv_len, float descale_q, float descale_k,
+                       float descale_v, void* stream) {
+  int st = check_shape(B, H, N, d, scale);
+  if (st != FA_OK) return st;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  for (float f : {descale_q, descale_k, descale_v})
+    if (!isfinite(f) || !(f > 0.f)) return FA_ERR_INVALID_ARG;
+  if (!isfinite(scale * descale_q * descale_k)) return FA_ERR_INVALID_ARG;
+  const size_t ebytes = (size_t)B * H * N * d;
+  const size_t lbytes = (size_t)B * H * N * sizeof(float);
+  const void* in_p[3] = {Q8, K8, Vt8};
+  const Span in[3] = {span(Q8, ebytes), span(K8, ebytes), span(Vt8, ebytes)};
+  const void* out_p[2] = {O, LSE};
+  const Span out[2] = {span(O, 2 * ebytes), span(LSE, lbytes)};
+  st = check_ptrs(in, in_p, 3, out, out_p, 2);
+  if (st != FA_OK) return st;
+  const fa::AttnShape s{B, H, N, d, scale, causal, kv_len};
+  return hip_status(fa::launch_fwd_fp8(Q8, K8, Vt8, O, LSE, s, descale_q, descale_k, descale_v,
+                                       static_cast<hipStream_t>(stream)));
+}
+
 int flash_attn_dropout_mask(uint8_t* mask, int B, int H, int N_q, int N_k, float p_drop, uint64_t seed,
                             uint32_t offset, void* stream) {
   fa::DropParams dp;

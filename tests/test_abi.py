@@ -224,3 +224,25 @@ def _fwd_sparse(lib, N=256, d=64, mask=FAKE + (1 << 24), stride=0, ptrs=None):
 ])
 def test_block_sparse_rejects(lib, kw, status):
     assert _fwd_sparse(lib, **kw) == status
+
+
+def _fwd_fp8(lib, N=64, d=64, dq=0.01, dk=0.01, dv=0.01, ptrs=None):
+    span = N * d * 2 + 4096
+    base = [FAKE + i * ((span + 4095) // 4096 * 4096) for i in range(5)]
+    if ptrs:
+        base = [ptrs.get(i, b) for i, b in enumerate(base)]
+    return lib.flash_attn_fwd_fp8(*[ctypes.c_void_p(x) if x is not None else None for x in base],
+                                  1, 1, N, d, 0.125, 0, None, dq, dk, dv, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dq=0.0), fa.binding.FA_ERR_INVALID_ARG),
+    (dict(dk=-1.0), fa.binding.FA_ERR_INVALID_ARG),
+    (dict(dv=math.nan), fa.binding.FA_ERR_INVALID_ARG),
+    (dict(dq=1e30, dk=1e30), fa.binding.FA_ERR_INVALID_ARG),
+    (dict(d=80), fa.binding.FA_ERR_UNSUPPORTED),
+    (dict(ptrs={2: None}), fa.binding.FA_ERR_INVALID_ARG),
+    (dict(ptrs={3: FAKE}), fa.binding.FA_ERR_INVALID_ARG),
+])
+def test_fp8_rejects(lib, kw, status):
+    assert _fwd_fp8(lib, **kw) == status
