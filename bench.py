@@ -16,8 +16,9 @@ timed the same way and reported under "workloads", next to the decoding
 forward (one new query per head against a 32K-slot cache), which is
 memory-bound and reported as an HBM rate, and the N=4096, d=128 workload
 again with fused dropout at p = 0.1 (same FLOP count; the generator work is
-not counted), and the block-sparse forward on a 64K-long sequence (FLOPs
-over the visible pairs of its block mask). Only one GPU is used.
+not counted), the block-sparse forward on a 64K-long sequence (FLOPs
+over the visible pairs of its block mask), and the 8-bit (E4M3) forward on
+the N=4096, d=128 shape. Only one GPU is used.
 """
 from __future__ import annotations
 
@@ -33,6 +34,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 matrix-core peak (2.5 PFLOP/s class)
 PEAK_HBM_TBPS = 8.0        # MI355X HBM3E peak
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense FP8 matrix-core peak
 PRIMARY = "gpt2_medium"
 DROPOUT_SEED = 0x5EED  # generator key of the dropout workload
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -240,6 +242,41 @@ def block_sparse_case(steps, warmup):
             "fwd_tflops": round(tflops, 2), "fwd_frac": round(tflops / PEAK_BF16_TFLOPS, 4)}
 
 
+def fp8_case(steps, warmup):
+    """The 8-bit forward on the N=4096, d=128 workload quantised to E4M3:
+    time per call from events on the stream and TFLOP/s (4 d per pair), as a
+    fraction of the MI355X dense FP8 matrix-core peak."""
+    import torch
+    import io_aware_exact_11_amd as fa
+    from io_aware_exact_11_amd import workloads as wl
+    name = "n4096_d128_fp8"
+    c = wl.FP8_WORKLOADS[name]
+    B, H, N, d = c["B"], c["H"], c["N"], c["d"]
+    x = wl.make_fp8_inputs(B, H, N, d, c["seed"], c["qkv_scale"])
+    q8, k8, vt8 = (torch.from_numpy(x[n]).cuda() for n in ("Q8", "K8", "Vt8"))
+    dq, dk, dv = x["dq"], x["dk"], x["dv"]
+    del x
+    o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    scale = float(d) ** -0.5
+    for _ in range(warmup):
+        fa.flash_attn_fwd_fp8(q8, k8, vt8, dq, dk, dv, causal=c["causal"], scale=scale, out=o, lse=lse)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        fa.flash_attn_fwd_fp8(q8, k8, vt8, dq, dk, dv, causal=c["causal"], scale=scale, out=o, lse=lse)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    pairs = B * H * (N * (N + 1) // 2 if c["causal"] else N * N)
+    tflops = 4 * d * pairs / (ms * 1e-3) / 1e12
+    return {"workload": name, "kind": "fp8 (E4M3) forward", "B": B, "H": H, "N": N, "d": d, "causal": c["causal"],
+            "ms_per_call": round(ms, 4), "fwd_tflops": round(tflops, 2),
+            "fwd_frac_of_fp8_peak": round(tflops / PEAK_FP8_TFLOPS, 4),
+            "fwd_frac_of_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4)}
+
+
 def memory_sweep():
     """Peak device memory of one fwd+bwd step (inputs, outputs, workspace) at
     B=2, H=16, d=128, causal, for growing N: grows linearly in N."""
@@ -353,6 +390,8 @@ def main():
             torch.cuda.empty_cache()
         extra.append(decode_case(args.steps, args.warmup))
         extra.append(block_sparse_case(args.steps, args.warmup))
+        torch.cuda.empty_cache()
+        extra.append(fp8_case(args.steps, args.warmup))
         torch.cuda.empty_cache()
         result["workloads"] = extra
         result["memory_sweep_B2_H16_d128_causal"] = memory_sweep()
