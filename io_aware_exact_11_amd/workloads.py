@@ -19,6 +19,12 @@ Decoding inputs (``make_decode_inputs``) follow the same recipe with Q of
 shape [B, H, Nq, d] and K, V of shape [B, H, Nk, d] (no dO), then, when
 ragged, one cache length per batch row kv_len[b] ~ U{Nk/2 .. Nk}.
 
+8-bit inputs (``make_fp8_inputs``) draw Q, K, V the same way and quantise
+each tensor to FP8 E4M3 with torch's float8_e4m3fn conversion after
+dividing it by its largest magnitude / 448; V is returned transposed.
+Block-sparse masks (``block_sparse_pattern``) are a band of blocks around
+the diagonal plus the first key block.
+
 The shapes follow the pages' workloads: the GPT-2-medium attention shape
 (FlashAttention does more arithmetic to move less data, section
 "FlashAttention never writes the full score table to HBM"), the N=4096,
