@@ -201,8 +201,9 @@ int flash_attn_fwd_block_sparse(const void* Q, const void* K, const void* V, voi
  * Q = descale_q * Q8, K = descale_k * K8, V = descale_v * Vt8^T (fp32 factors,
  * finite and > 0). O (bf16, [B, H, N, d]) and LSE (fp32, natural log) are
  * the attention of those values: scores and softmax in fp32, the softmax
- * weights rounded to E4M3 for the P V product. Other arguments and
- * conventions as flash_attn_fwd. */
+ * weights rounded to E4M3 for the P V product. N must be a multiple of 4
+ * (the rows of Vt8 then start on 4-byte boundaries); other N is
+ * FA_ERR_UNSUPPORTED. Other arguments and conventions as flash_attn_fwd. */
 int flash_attn_fwd_fp8(const void* Q8, const void* K8, const void* Vt8, void* O, float* LSE, int B, int H, int N,
                        int d, float scale, int causal, const int32_t* kv_len, float descale_q, float descale_k,
                        float descale_v, void* stream);

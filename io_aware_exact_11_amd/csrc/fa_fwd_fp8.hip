@@ -13,7 +13,11 @@
 // One workgroup owns 128 query rows (4 waves of 32) and streams 64-key
 // tiles: K as [64 keys][d] and V^T as [d][64 keys], byte tiles padded so the
 // 32-byte operand reads of 16 consecutive rows fall in distinct banks, moved
-// by direct buffer-to-LDS loads and double-buffered.
+// by direct buffer-to-LDS loads and double-buffered. V^T rows are N bytes,
+// so a tile row's 16-byte loads run into the next row (keys >= N get zero
+// weight) and, for the last row, past the head's range, which reads zeros
+// dword by dword; N is a multiple of 4 (checked on the host) so that no
+// dword straddles that end.
 //
 // Operand bytes: the instruction pairs byte b of lane group g in A with
 // byte b of lane group g in B (both map it to the same k index), so

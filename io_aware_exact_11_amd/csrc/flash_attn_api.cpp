@@ -244,6 +244,9 @@ int flash_attn_fwd_fp8(const void* Q8, const void* K8, const void* Vt8, void* O,
   for (float f : {descale_q, descale_k, descale_v})
     if (!isfinite(f) || !(f > 0.f)) return FA_ERR_INVALID_ARG;
   if (!isfinite(scale * descale_q * descale_k)) return FA_ERR_INVALID_ARG;
+  // V^T rows are N bytes long: a multiple of 4 keeps every row dword-aligned,
+  // so no 16-byte tile load straddles the end of a head's range.
+  if (N % 4 != 0) return FA_ERR_UNSUPPORTED;
   const size_t ebytes = (size_t)B * H * N * d;
   const size_t lbytes = (size_t)B * H * N * sizeof(float);
   const void* in_p[3] = {Q8, K8, Vt8};

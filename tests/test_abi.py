@@ -241,6 +241,8 @@ def _fwd_fp8(lib, N=64, d=64, dq=0.01, dk=0.01, dv=0.01, ptrs=None):
     (dict(dv=math.nan), fa.binding.FA_ERR_INVALID_ARG),
     (dict(dq=1e30, dk=1e30), fa.binding.FA_ERR_INVALID_ARG),
     (dict(d=80), fa.binding.FA_ERR_UNSUPPORTED),
+    (dict(N=63), fa.binding.FA_ERR_UNSUPPORTED),
+    (dict(N=1), fa.binding.FA_ERR_UNSUPPORTED),
     (dict(ptrs={2: None}), fa.binding.FA_ERR_INVALID_ARG),
     (dict(ptrs={3: FAKE}), fa.binding.FA_ERR_INVALID_ARG),
 ])

@@ -91,3 +91,34 @@ def test_full_size_sparse_64k_workload():
         ro, rl = bs.forward_rows_block_sparse(x["Q"][0, h], x["K"][0, h], x["V"][0, h], rows, scale, bm, w["causal"])
         compare("O", host(O[0, h][torch.from_numpy(rows).cuda()]), ro)
         compare_lse(host(lse[0, h][torch.from_numpy(rows).cuda()]), rl)
+
+
+@pytest.mark.parametrize("N,d,causal", [(1, 64, False), (1, 128, True), (127, 128, False), (129, 64, True)])
+def test_block_sparse_edge_lengths(N, d, causal):
+    from oracle import block_sparse as bs
+    from tests.gpu_util import compare, compare_lse, dev_bf16, host, log
+    fa = _fa()
+    log(f"  sparse edge N={N} d={d} causal={causal}")
+    x = wl.make_inputs(1, 2, N, d, seed=21 + N)
+    nb = (N + 127) // 128
+    bm = np.ones((nb, nb), np.uint8)
+    if nb > 1:
+        bm[1, 0] = 0
+    q, k, v = (dev_bf16(x[n + "_bits"]) for n in ("Q", "K", "V"))
+    scale = float(np.float32(d ** -0.5))
+    O, lse = fa.flash_attn_fwd_block_sparse(q, k, v, torch.from_numpy(bm).cuda(), causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    Ro, Rl = bs.forward_block_sparse(x["Q"], x["K"], x["V"], scale, bm, causal)
+    compare("O", host(O), Ro)
+    compare_lse(host(lse), Rl)
+
+
+def test_block_sparse_kv_len_zero_row():
+    from tests.gpu_util import dev_bf16
+    fa = _fa()
+    x = wl.make_inputs(2, 1, 256, 128, seed=22)
+    q, k, v = (dev_bf16(x[n + "_bits"]) for n in ("Q", "K", "V"))
+    kv = torch.tensor([0, 200], dtype=torch.int32, device="cuda")
+    O, lse = fa.flash_attn_fwd_block_sparse(q, k, v, torch.ones(2, 2, dtype=torch.uint8, device="cuda"), kv_len=kv)
+    torch.cuda.synchronize()
+    assert torch.all(O[0] == 0) and torch.all(torch.isneginf(lse[0])) and torch.all(torch.isfinite(lse[1]))

@@ -189,3 +189,37 @@ def test_reproducible_and_offset_draws_new_mask():
     c, _ = fa.flash_attn_fwd_dropout(dev["Q"], dev["K"], dev["V"], 0.2, 1, 1)
     assert torch.equal(a, b)
     assert not torch.equal(a, c)
+
+
+@pytest.mark.parametrize("N,d,causal", [(1, 64, False), (1, 128, True), (63, 128, False), (65, 64, True),
+                                        (129, 128, True)])
+def test_dropout_edge_lengths(N, d, causal):
+    from oracle import dropout as od
+    from tests.gpu_util import compare, compare_lse, host, log
+    fa = _fa()
+    log(f"  dropout edge N={N} d={d} causal={causal}")
+    x, dev, _ = _inputs(1, 2, N, d, seed=3 + N)
+    scale = float(np.float32(d ** -0.5))
+    O, lse = fa.flash_attn_fwd_dropout(dev["Q"], dev["K"], dev["V"], 0.3, 77, 1, causal=causal, scale=scale)
+    g = fa.flash_attn_bwd_dropout(dev["Q"], dev["K"], dev["V"], O, dev["dO"], lse, 0.3, 77, 1, causal=causal,
+                                  scale=scale)
+    torch.cuda.synchronize()
+    Ro, Rl = od.forward_dropout(x["Q"], x["K"], x["V"], scale, 0.3, 77, 1, causal)
+    Rg = od.backward_dropout(x["Q"], x["K"], x["V"], x["dO"], scale, 0.3, 77, 1, causal)
+    compare("O", host(O), Ro)
+    compare_lse(host(lse), Rl)
+    for nm, a, b in zip(("dQ", "dK", "dV"), g, Rg):
+        compare(nm, host(a), b)
+
+
+def test_dropout_kv_len_zero_rows():
+    """A batch row with kv_len = 0 has no visible key: O = 0, LSE = -inf, zero gradients."""
+    fa = _fa()
+    x, dev, _ = _inputs(2, 2, 96, 64, seed=12)
+    kv = torch.tensor([0, 96], dtype=torch.int32, device="cuda")
+    O, lse = fa.flash_attn_fwd_dropout(dev["Q"], dev["K"], dev["V"], 0.2, 5, 0, kv_len=kv)
+    dQ, dK, dV = fa.flash_attn_bwd_dropout(dev["Q"], dev["K"], dev["V"], O, dev["dO"], lse, 0.2, 5, 0, kv_len=kv)
+    torch.cuda.synchronize()
+    assert torch.all(O[0] == 0) and torch.all(torch.isneginf(lse[0]))
+    assert torch.all(dQ[0] == 0) and torch.all(dK[0] == 0) and torch.all(dV[0] == 0)
+    assert torch.all(torch.isfinite(lse[1]))

@@ -58,8 +58,9 @@ def _check_head(O, L, q8, k8, vt8, dq, dk, dv, scale, causal, kv_len, rows=None)
     compare_lse(L, Rl)
 
 
-CASES = [(1, 2, 200, 64, False, False), (2, 2, 256, 128, False, False), (2, 2, 333, 128, True, False),
-         (2, 2, 384, 64, True, True), (1, 3, 129, 128, False, True), (1, 2, 1024, 128, True, False)]
+# N is a multiple of 4 (the entry point's requirement), ragged against the 64-key tiles.
+CASES = [(1, 2, 200, 64, False, False), (2, 2, 256, 128, False, False), (2, 2, 332, 128, True, False),
+         (2, 2, 384, 64, True, True), (1, 3, 132, 128, False, True), (1, 2, 1024, 128, True, False)]
 
 
 @pytest.mark.parametrize("B,H,N,d,causal,padded", CASES)
@@ -132,3 +133,35 @@ def test_full_size_n4096_d128_fp8_workload():
     for b, h in ((0, 0), (7, 9), (15, 15)):
         _check_head(host(O[b, h][ridx]), host(L[b, h][ridx]), x["Q8"][b, h], x["K8"][b, h], x["Vt8"][b, h],
                     x["dq"], x["dk"], x["dv"], scale, w["causal"], None, rows=rows)
+
+
+@pytest.mark.parametrize("N,d,causal", [(4, 64, False), (4, 128, True), (60, 128, False), (68, 64, True),
+                                        (124, 128, False)])
+def test_fp8_edge_lengths(N, d, causal):
+    from tests.gpu_util import host, log
+    fa = _fa()
+    log(f"  fp8 edge N={N} d={d} causal={causal}")
+    x = wl.make_fp8_inputs(1, 2, N, d, seed=31 + N)
+    scale = float(np.float32(d ** -0.5))
+    O, L = fa.flash_attn_fwd_fp8(_dev(x["Q8"]), _dev(x["K8"]), _dev(x["Vt8"]), x["dq"], x["dk"], x["dv"],
+                                 causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    for h in range(2):
+        _check_head(host(O)[0, h], host(L)[0, h], x["Q8"][0, h], x["K8"][0, h], x["Vt8"][0, h], x["dq"], x["dk"],
+                    x["dv"], scale, causal, None)
+
+
+def test_fp8_kv_len_zero_row():
+    fa = _fa()
+    x = wl.make_fp8_inputs(2, 1, 132, 128, seed=33)
+    kv = torch.tensor([0, 100], dtype=torch.int32, device="cuda")
+    O, L = fa.flash_attn_fwd_fp8(_dev(x["Q8"]), _dev(x["K8"]), _dev(x["Vt8"]), x["dq"], x["dk"], x["dv"], kv_len=kv)
+    torch.cuda.synchronize()
+    assert torch.all(O[0] == 0) and torch.all(torch.isneginf(L[0])) and torch.all(torch.isfinite(L[1]))
+
+
+def test_fp8_rejects_length_not_multiple_of_4():
+    fa = _fa()
+    x = wl.make_fp8_inputs(1, 1, 63, 64, seed=34)
+    with pytest.raises(fa.FlashAttnError):
+        fa.flash_attn_fwd_fp8(_dev(x["Q8"]), _dev(x["K8"]), _dev(x["Vt8"]), x["dq"], x["dk"], x["dv"])
