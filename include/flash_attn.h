@@ -187,8 +187,10 @@ int flash_attn_dropout_mask(uint8_t* mask, int B, int H, int N_q, int N_k, float
  * block_mask[i/128][j/128] != 0, in addition to kv_len and causal; O and
  * LSE are the exact softmax attention over the visible keys (O = 0,
  * LSE = -inf for a row with none). Only key tiles of non-zero blocks are
- * read from memory. N <= 65536 (larger: FA_ERR_UNSUPPORTED); NULL mask or a
- * negative stride: FA_ERR_INVALID_ARG; other arguments as flash_attn_fwd. */
+ * read from memory. The masks occupy (B*H - 1) * block_mask_head_stride +
+ * nb * nb bytes, which must not overlap O or LSE. N <= 65536 (larger:
+ * FA_ERR_UNSUPPORTED); NULL mask, a negative stride or an overlap:
+ * FA_ERR_INVALID_ARG; other arguments as flash_attn_fwd. */
 int flash_attn_fwd_block_sparse(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
                                 int N, int d, float scale, int causal, const int32_t* kv_len,
                                 const uint8_t* block_mask, int64_t block_mask_head_stride, void* stream);

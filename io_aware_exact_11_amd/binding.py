@@ -98,6 +98,9 @@ def _check(name, t, dtype, shape):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be on the GPU")
+    if t.device.index != torch.cuda.current_device():
+        # the library launches on the current device and its current stream
+        raise ValueError(f"{name} is on {t.device}, but the current device is cuda:{torch.cuda.current_device()}")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if tuple(t.shape) != tuple(shape):

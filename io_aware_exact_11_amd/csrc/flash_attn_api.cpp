@@ -230,6 +230,13 @@ int flash_attn_fwd_block_sparse(const void* Q, const void* K, const void* V, voi
   if (st != FA_OK) return st;
   if (!block_mask || block_mask_head_stride < 0) return FA_ERR_INVALID_ARG;
   if (N > 65536) return FA_ERR_UNSUPPORTED;
+  // The masks span (B*H - 1) * stride + nb^2 bytes and must not overlap an output.
+  const int64_t nb = (N + 127) / 128, heads = (int64_t)B * H;
+  if (block_mask_head_stride > 0 && heads - 1 > (INT64_MAX - nb * nb) / block_mask_head_stride)
+    return FA_ERR_INVALID_ARG;
+  const Span mask = span(block_mask, (size_t)((heads - 1) * block_mask_head_stride + nb * nb));
+  const size_t obytes = (size_t)B * H * N * d * 2, lbytes = (size_t)B * H * N * sizeof(float);
+  if (overlaps(mask, span(O, obytes)) || overlaps(mask, span(LSE, lbytes))) return FA_ERR_INVALID_ARG;
   const fa::AttnShape s{B, H, N, d, scale, causal, kv_len};
   return hip_status(fa::launch_fwd_sparse_bf16(Q, K, V, O, LSE, s, block_mask, (long long)block_mask_head_stride,
                                                static_cast<hipStream_t>(stream)));

@@ -204,11 +204,13 @@ def test_dropout_mask_rejects_invalid(lib, args):
         fa.binding.FA_ERR_INVALID_ARG
 
 
-def _fwd_sparse(lib, N=256, d=64, mask=FAKE + (1 << 24), stride=0, ptrs=None):
+def _fwd_sparse(lib, N=256, d=64, mask=FAKE + (1 << 24), stride=0, ptrs=None, mask_in=None):
     span = 1 * 1 * N * 128 * 2 + 4096
     base = [FAKE + i * ((span + 4095) // 4096 * 4096) for i in range(5)]
     if ptrs:
         base = [ptrs.get(i, b) for i, b in enumerate(base)]
+    if mask_in is not None:  # the mask placed inside tensor mask_in (3 = O, 4 = LSE)
+        mask = base[mask_in] + 64
     return lib.flash_attn_fwd_block_sparse(*[ctypes.c_void_p(x) if x is not None else None for x in base],
                                            1, 1, N, d, 0.125, 0, None,
                                            ctypes.c_void_p(mask) if mask else None, stride, None)
@@ -221,6 +223,8 @@ def _fwd_sparse(lib, N=256, d=64, mask=FAKE + (1 << 24), stride=0, ptrs=None):
     (dict(d=96), fa.binding.FA_ERR_UNSUPPORTED),
     (dict(ptrs={1: None}), fa.binding.FA_ERR_INVALID_ARG),
     (dict(ptrs={3: FAKE}), fa.binding.FA_ERR_INVALID_ARG),
+    (dict(mask_in=3), fa.binding.FA_ERR_INVALID_ARG),
+    (dict(mask_in=4), fa.binding.FA_ERR_INVALID_ARG),
 ])
 def test_block_sparse_rejects(lib, kw, status):
     assert _fwd_sparse(lib, **kw) == status
