@@ -54,12 +54,13 @@ def pairs_per_batch(w, causal, kv_len):
 
 
 def kernel_source_digest():
-    """Digest of the kernel sources with comments and blank lines removed, so
-    that stored counter results stay valid across comment-only edits."""
+    """Digest of the device sources (.h, .hip) with comments and blank lines
+    removed, so that stored counter results stay valid across comment-only
+    edits and changes to the host-side entry points."""
     import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "io_aware_exact_11_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in sorted(n for n in os.listdir(csrc) if n.endswith((".h", ".hip"))):
         with open(os.path.join(csrc, name), encoding="utf-8") as f:
             text = f.read()
         lines = (re.sub(r"//.*", "", ln).rstrip() for ln in text.splitlines())
