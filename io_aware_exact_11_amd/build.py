@@ -25,8 +25,12 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # default heuristic parks them in AGPRs and copies them back and forth around
 # every product in the register-heavy backward kernels.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
-         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-         "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+_VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+# Units built with the compiler's default (AGPR) accumulator form: the
+# atomic-dQ key-outer kernel, whose precise d=128 instance crashes the
+# compiler's AGPR-copy rewrite in the VGPR form.
+AGPR_FORM_SOURCES = {"fa_bwd_dkdv_atomic.hip"}
 # Per-source instruction-scheduling strategy (the compiler's default where
 # absent), chosen by measurement on MI355X. At d=128 the default scheduler
 # issues each LDS operand read right before the product that consumes it and
@@ -55,7 +59,8 @@ def build(verbose: bool = False) -> str:
     for src in SOURCES:
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
-        cmds.append([HIPCC, *FLAGS, *SOURCE_FLAGS.get(src, []), "-I", os.path.join(PKG, "..", "include"), "-c",
+        form = [] if src in AGPR_FORM_SOURCES else _VGPR_FORM
+        cmds.append([HIPCC, *FLAGS, *form, *SOURCE_FLAGS.get(src, []), "-I", os.path.join(PKG, "..", "include"), "-c",
                      os.path.join(CSRC, src), "-o", obj])
     with cf.ThreadPoolExecutor(max_workers=min(8, len(cmds))) as ex:
         for cmd, msg in zip(cmds, ex.map(_run, cmds)):

@@ -221,11 +221,9 @@ struct DkdvCfg {
   static constexpr int NW = 4;
   static constexpr int BKV = 32 * NW;          // keys per workgroup (32 per wave)
   static constexpr int BQ = 64;                // query rows per block
-  // Q and dO tile row stride (elements): both tiles are read row-wise
-  // (16-byte reads, 16 rows per read group) and transposed (4 rows x 4
-  // eight-byte columns); a row step of 12 banks (d=128) or 52 banks (d=64),
-  // mod 64, keeps both patterns conflict-free.
-  static constexpr int QSTR = D == 128 ? D + 24 : D + 40;
+  // Q and dO tile row stride (elements) of the xpad layout (xpad_off): both
+  // tiles are read row-wise and transposed, conflict-free in that layout.
+  static constexpr int QSTR = D + 32;
   static constexpr int KCH = BKV * D / 8 / 256;
   static constexpr int DSTR = BKV + 8;         // dS tile row stride (row reads only)
 };
@@ -324,8 +322,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     // Block q0: Q and dO rows straight into LDS; this thread's row
     // statistics raw into registers (scaled when stored).
     auto load = [&](int q0, u16* Qt, u16* Gt) {
-      tile_to_lds_padded<D, QSTR, BQ, C::NW>(rQ, q0, Qt, w, lane);
-      tile_to_lds_padded<D, QSTR, BQ, C::NW>(rO, q0, Gt, w, lane);
+      tile_to_lds_xpad<D, QSTR, BQ, C::NW>(rQ, q0, Qt, w, lane);
+      tile_to_lds_xpad<D, QSTR, BQ, C::NW>(rO, q0, Gt, w, lane);
       qrow = q0 + (tid & (BQ - 1));
       lraw = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rL, (unsigned)qrow * 4, 0, 0));
       draw = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rD, (unsigned)qrow * 4, 0, 0));
@@ -342,6 +340,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     // 16 * ((lane / 16) % 2) + 4 * (lane % 4) inside a 32-column tile.
     const int tr_row = 4 * g + ((lane & 15) >> 2);
     const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    // This lane's offsets in the xpad tiles. Row-wise: chunk 2kk + g of row
+    // 32qt + r is at rw[kk % 2] + 32qt*QSTR + 32(kk / 2) (bits 2..3 of the row
+    // are those of r). Transposed: columns 32t + tr_col of rows
+    // 16c + tr_row + 8j are at tw[j] + 16c*QSTR + 32t (bits 2..3 of those
+    // rows are g + 2j).
+    const int xr = (r >> 2) & 3;
+    const int rw0 = r * QSTR + 8 * (g ^ xr), rw1 = r * QSTR + 8 * ((2 + g) ^ xr);
+    const int tw0 = tr_row * QSTR + 8 * ((tr_col >> 3) ^ g) + (tr_col & 7);
+    const int tw1 = (tr_row + 8) * QSTR + 8 * ((tr_col >> 3) ^ g ^ 2) + (tr_col & 7);
 
     load(qb_start * BQ, Q0, G0);
     wait_vmem_all();
@@ -361,13 +368,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
         f32x16 sa[BQ / 32], pa[BQ / 32];
 #pragma unroll
         for (int qt = 0; qt < BQ / 32; ++qt) {
-          const int row = 32 * qt + r;
-          sa[qt] = mfma32_first(ld_lds16(Qt + row * QSTR + 8 * g), kf[0]);
-          pa[qt] = mfma32_first(ld_lds16(Gt + row * QSTR + 8 * g), vf[0]);
+          const int rb = 32 * qt * QSTR;
+          sa[qt] = mfma32_first(ld_lds16(Qt + rb + rw0), kf[0]);
+          pa[qt] = mfma32_first(ld_lds16(Gt + rb + rw0), vf[0]);
 #pragma unroll
           for (int kk = 1; kk < D / 16; ++kk) {
-            sa[qt] = mfma32(ld_lds16(Qt + row * QSTR + 16 * kk + 8 * g), kf[kk], sa[qt]);
-            pa[qt] = mfma32(ld_lds16(Gt + row * QSTR + 16 * kk + 8 * g), vf[kk], pa[qt]);
+            const int o = rb + 32 * (kk >> 1) + ((kk & 1) ? rw1 : rw0);
+            sa[qt] = mfma32(ld_lds16(Qt + o), kf[kk], sa[qt]);
+            pa[qt] = mfma32(ld_lds16(Gt + o), vf[kk], pa[qt]);
           }
         }
         // Masked scores become -inf, so their weights come out exactly 0.
@@ -426,9 +434,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
         for (int t = 0; t < D / 32; ++t)
 #pragma unroll
           for (int c = 0; c < BQ / 16; ++c) {
-            const int r0 = 16 * c + tr_row, col = 32 * t + tr_col;
-            const bf16x8 aO = join_tr(ld_lds_tr(Gt + r0 * QSTR + col), ld_lds_tr(Gt + (r0 + 8) * QSTR + col));
-            const bf16x8 aQ = join_tr(ld_lds_tr(Qt + r0 * QSTR + col), ld_lds_tr(Qt + (r0 + 8) * QSTR + col));
+            const int o = 16 * c * QSTR + 32 * t;
+            const bf16x8 aO = join_tr(ld_lds_tr(Gt + o + tw0), ld_lds_tr(Gt + o + tw1));
+            const bf16x8 aQ = join_tr(ld_lds_tr(Qt + o + tw0), ld_lds_tr(Qt + o + tw1));
             dv[t] = mfma32(aO, pb[c], dv[t]);
             dk[t] = mfma32(aQ, db[c], dk[t]);
             if constexpr (PRECISE) {
@@ -523,11 +531,10 @@ struct DqCfg {
   static constexpr int NW = 4;
   static constexpr int BR = 32 * NW;           // query rows per workgroup
   static constexpr int BC = 64;                // keys per tile
-  // LDS row strides (elements). K is read row-wise (16-byte reads, 16 rows
-  // per read group) and transposed (4 rows x 4 eight-byte columns): a row
-  // step of 12 banks (mod 64) keeps both conflict-free. V is read row-wise
-  // only: a step of 4 banks.
-  static constexpr int KSTR = D == 128 ? D + 24 : D + 8;
+  // LDS row strides (elements). K is read row-wise and transposed, from an
+  // xpad tile (xpad_off), conflict-free for both. V is read row-wise only:
+  // a padded step of 4 banks.
+  static constexpr int KSTR = D + 32;
   static constexpr int VSTR = D + 8;
 };
 
@@ -626,11 +633,19 @@ __global__ __launch_bounds__(256, PRECISE ? 1 : 2) void bwd_dq_kernel(
     for (int e = 0; e < 16; ++e) acc[t][e] = 0.f;
 
   auto load = [&](int kb, u16* Kt, u16* Vt) {
-    tile_to_lds_padded<D, KSTR, BC, C::NW>(rK, kb, Kt, w, lane);
+    tile_to_lds_xpad<D, KSTR, BC, C::NW>(rK, kb, Kt, w, lane);
     tile_to_lds_padded<D, VSTR, BC, C::NW>(rV, kb, Vt, w, lane);
   };
   const int tr_row = 4 * g + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  // This lane's offsets in the xpad K tile, as in the dK/dV kernel: row-wise
+  // chunk 2kk + g of row 32mt + r at rw[kk % 2] + 32mt*KSTR + 32(kk / 2);
+  // transposed columns 32t + tr_col of rows 16c + tr_row + 8j at
+  // tw[j] + 16c*KSTR + 32t.
+  const int xr = (r >> 2) & 3;
+  const int rw0 = r * KSTR + 8 * (g ^ xr), rw1 = r * KSTR + 8 * ((2 + g) ^ xr);
+  const int tw0 = tr_row * KSTR + 8 * ((tr_col >> 3) ^ g) + (tr_col & 7);
+  const int tw1 = (tr_row + 8) * KSTR + 8 * ((tr_col >> 3) ^ g ^ 2) + (tr_col & 7);
 
   if (nt > 0) load(0, K0, V0);
   wait_vmem_all();
@@ -647,11 +662,11 @@ __global__ __launch_bounds__(256, PRECISE ? 1 : 2) void bwd_dq_kernel(
 #pragma unroll
       for (int mt = 0; mt < BC / 32; ++mt) {
         const int row = 32 * mt + r;
-        s[mt] = mfma32_first(ld_lds16(Kc + row * KSTR + 8 * g), qf[0]);
+        s[mt] = mfma32_first(ld_lds16(Kc + 32 * mt * KSTR + rw0), qf[0]);
         dp[mt] = mfma32_first(ld_lds16(Vc + row * VSTR + 8 * g), df[0]);
 #pragma unroll
         for (int kk = 1; kk < D / 16; ++kk) {
-          s[mt] = mfma32(ld_lds16(Kc + row * KSTR + 16 * kk + 8 * g), qf[kk], s[mt]);
+          s[mt] = mfma32(ld_lds16(Kc + 32 * mt * KSTR + 32 * (kk >> 1) + ((kk & 1) ? rw1 : rw0)), qf[kk], s[mt]);
           dp[mt] = mfma32(ld_lds16(Vc + row * VSTR + 16 * kk + 8 * g), df[kk], dp[mt]);
         }
       }
@@ -692,8 +707,8 @@ __global__ __launch_bounds__(256, PRECISE ? 1 : 2) void bwd_dq_kernel(
       for (int t = 0; t < D / 32; ++t)
 #pragma unroll
         for (int c = 0; c < BC / 16; ++c) {
-          const int r0 = 16 * c + tr_row, col = 32 * t + tr_col;
-          const bf16x8 aK = join_tr(ld_lds_tr(Kc + r0 * KSTR + col), ld_lds_tr(Kc + (r0 + 8) * KSTR + col));
+          const int o = 16 * c * KSTR + 32 * t;
+          const bf16x8 aK = join_tr(ld_lds_tr(Kc + o + tw0), ld_lds_tr(Kc + o + tw1));
           acc[t] = mfma32(aK, db[c], acc[t]);
           if constexpr (PRECISE) acc[t] = mfma32(aK, dl[c], acc[t]);
         }

@@ -199,6 +199,68 @@ __device__ __forceinline__ void tile_to_lds_padded(__amdgpu_buffer_rsrc_t rs, in
   }
 }
 
+// Tiles read both by rows and transposed. With 64 four-byte banks, a 16-byte
+// row read serves 16 consecutive rows per LDS cycle, so those rows must
+// start in 16 distinct 4-bank groups; a transposing read (ds_read_b64_tr_b16)
+// serves 4 consecutive rows x 4 adjacent chunks per 32 lanes, so those rows
+// must start 16 banks apart. No row padding satisfies both. The "xpad"
+// layout pads each row to a 16-bank step (S*2 bytes = 64 or 192 mod 256)
+// and stores chunk c of row r at chunk c ^ ((r >> 2) & 3): the XOR only
+// permutes the four chunks of each 64-byte group, so the transposing read
+// keeps its four rows in distinct 16-bank quarters and the row read spreads
+// 16 consecutive rows over all 16 groups.
+template <int S>
+__device__ __forceinline__ constexpr int xpad_off(int row, int chunk) {
+  return row * S + 8 * (chunk ^ ((row >> 2) & 3));
+}
+
+// Direct-to-LDS copy of ROWS rows of D bf16 into an xpad tile of row stride
+// S elements (see xpad_off). Lane l of block blk fills tile byte
+// 1024*blk + 16*l: it fetches the global chunk that the XOR places there
+// (the map is its own inverse); lanes that land in the padding re-read the
+// row's first chunk. Rows past the end of the buffer resource read zeros.
+template <int D, int S, int ROWS, int NW>
+__device__ __forceinline__ void tile_to_lds_xpad(__amdgpu_buffer_rsrc_t rs, int row0, u16* tile, int w, int lane) {
+  static_assert((S * 2) % 256 == 64 || (S * 2) % 256 == 192, "16-bank row step");
+  static_assert(S >= D, "row fits");
+  constexpr int BYTES = ROWS * S * 2;
+  static_assert(BYTES % 1024 == 0, "whole 1 KB blocks");
+  constexpr int NBLK = BYTES / 1024;
+#pragma unroll
+  for (int i = 0; i < (NBLK + NW - 1) / NW; ++i) {
+    const int blk = w + NW * i;
+    if (NBLK % NW == 0 || blk < NBLK) {
+      const int off = blk * 1024 + lane * 16;
+      const int row = off / (S * 2), pc = (off % (S * 2)) >> 4;
+      const int src = (row0 + row) * D * 2 + (pc < D / 8 ? (pc ^ ((row >> 2) & 3)) * 16 : 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)(tile + blk * 512), 16, src, 0, 0, 0);
+    }
+  }
+}
+
+// Direct-to-LDS copy of ROWS rows of 128 bf16 into an unpadded tile that
+// is only read transposed (ds_read_b64_tr_b16: 4 consecutive rows x 4
+// adjacent chunks per 32 lanes). Chunk c of row r is stored at chunk
+// c ^ 4(r & 3), which puts those four rows in distinct 16-bank quarters of
+// the 64 four-byte banks. Lane l of block blk fills tile byte 1024*blk +
+// 16*l and fetches the global chunk placed there (the map is its own
+// inverse). Rows past the end of the buffer resource read zeros.
+template <int ROWS, int NW>
+__device__ __forceinline__ void tile_to_lds_trxor(__amdgpu_buffer_rsrc_t rs, int row0, u16* tile, int w, int lane) {
+  constexpr int D = 128;
+  constexpr int INST = ROWS * D * 2 / 1024;
+  static_assert(INST % NW == 0, "whole 1 KB blocks per wave");
+#pragma unroll
+  for (int i = 0; i < INST / NW; ++i) {
+    const int blk = w * (INST / NW) + i;
+    const int row = blk * 4 + (lane >> 4), pc = lane & 15;
+    const int src = (row0 + row) * D * 2 + ((pc ^ (4 * (row & 3))) << 4);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (__attribute__((address_space(3))) void*)(tile + blk * 512), 16, src, 0, 0, 0);
+  }
+}
+
 // Map a linear workgroup id to a tile id so that the tiles of one (b, h)
 // run on one XCD, in order: workgroups are dispatched round-robin over the
 // 8 XCDs, each with its own L2, and neighbouring tiles of a head share K, V.

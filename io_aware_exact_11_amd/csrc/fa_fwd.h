@@ -61,10 +61,12 @@ struct FwdCfg {
   static constexpr int BC = 64;                 // keys per tile
   static constexpr int KSTR = D + 8;            // K tile row stride (elements)
   // V tile row stride: the 4 rows of a transposing read must land in
-  // disjoint banks (16 banks apart at d=128; at d=64 a stride of D+8 already
-  // places them 36 banks apart, and the smaller tile lets four workgroups
-  // share a CU).
-  static constexpr int VSTR = D == 64 ? D + 8 : D + 32;
+  // disjoint banks. At d=64 a stride of D+8 places them 36 banks apart (and
+  // the smaller tile lets four workgroups share a CU). At d=128 the direct-
+  // to-LDS tile is unpadded and XOR-permuted instead (tile_to_lds_trxor):
+  // no padding to load; the register-staged d=128 tile keeps a 16-bank step.
+  static constexpr bool VXOR = D == 128 && DL_;
+  static constexpr int VSTR = D == 64 ? D + 8 : (VXOR ? D : D + 32);
   static constexpr int CH = BC * D / 8 / NT;    // 16-byte chunks per thread per tile
   static_assert(D == 64 || D == 128, "head dim");
   static_assert(CH * NT * 8 == BC * D, "tile split");
@@ -243,7 +245,12 @@ __global__ __launch_bounds__(C::NT, C::OCC * 4 / C::NW) void fwd_bf16_kernel(
   };
   // Per-lane offsets of the transposing V reads (see ld_lds_tr): row part
   // 4g + (lane % 16) / 4, column part 16 * ((lane / 16) % 2) + 4 * (lane % 4).
+  // In the XOR-permuted tile the 32-column group t of this lane's rows sits
+  // at group t ^ q, q = row % 4 = (lane / 4) % 4, the same for all its rows.
   const int v_tr_off = (4 * g + ((lane & 15) >> 2)) * C::VSTR + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  int v_grp[D / 32];
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t) v_grp[t] = C::VXOR ? 32 * (t ^ ((lane >> 2) & 3)) : 32 * t;
   // Causal waves compute only the tiles that reach their rows (a prefix).
   // Causal block-sparse: the listed tiles that reach this wave's rows (a
   // prefix of the ascending list).
@@ -334,7 +341,7 @@ __global__ __launch_bounds__(C::NT, C::OCC * 4 / C::NW) void fwd_bf16_kernel(
     for (int t = 0; t < D / 32; ++t)
 #pragma unroll
       for (int c = 0; c < BC / 16; ++c) {
-        const u16* vp = vb + (16 * c) * C::VSTR + 32 * t;
+        const u16* vp = vb + (16 * c) * C::VSTR + v_grp[t];
         const bf16x8 a = join_tr(ld_lds_tr(vp), ld_lds_tr(vp + 8 * C::VSTR));
 #pragma unroll
         for (int s = 0; s < QS; ++s) o[s][t] = mfma32(a, pb[s][c], o[s][t]);
@@ -342,6 +349,13 @@ __global__ __launch_bounds__(C::NT, C::OCC * 4 / C::NW) void fwd_bf16_kernel(
   };
 
   f32x16 s_cur[QS][BC / 32];
+  // Direct-to-LDS V tile load in the layout the reads above expect.
+  auto load_v_dl = [&](int kb, u16* Vt) {
+    if constexpr (C::VXOR)
+      tile_to_lds_trxor<BC, C::NW>(rV, kb, Vt, w, lane);
+    else
+      tile_to_lds_padded<D, C::VSTR, BC, C::NW>(rV, kb, Vt, w, lane);
+  };
   if constexpr (DL) {
     // K_j sits in Kd{j%2}, V_j in Vd{j%2}; K runs one tile ahead of V as
     // below. Each tile's loads go straight to LDS: K_{j+2} into the buffer
@@ -349,7 +363,7 @@ __global__ __launch_bounds__(C::NT, C::OCC * 4 / C::NW) void fwd_bf16_kernel(
     // that the buffer names are compile-time constants.
     if (nt > 0) {
       tile_to_lds_padded<D, C::KSTR, BC, C::NW>(rK, tnext(0, 0, 0), Kd0, w, lane);
-      tile_to_lds_padded<D, C::VSTR, BC, C::NW>(rV, tnext(0, 0, 0), Vd0, w, lane);
+      load_v_dl(tnext(0, 0, 0), Vd0);
     }
     if (nt > 1) tile_to_lds_padded<D, C::KSTR, BC, C::NW>(rK, tnext(0, 0, 1), Kd1, w, lane);
     wait_vmem_all();
@@ -361,7 +375,7 @@ __global__ __launch_bounds__(C::NT, C::OCC * 4 / C::NW) void fwd_bf16_kernel(
       constexpr bool P = decltype(odd)::value;
       const int kb = tnext(it, it * BC, 0);
       if (it + 2 < nt) tile_to_lds_padded<D, C::KSTR, BC, C::NW>(rK, tnext(it, kb, 2), P ? Kd1 : Kd0, w, lane);
-      if (it + 1 < nt) tile_to_lds_padded<D, C::VSTR, BC, C::NW>(rV, tnext(it, kb, 1), P ? Vd0 : Vd1, w, lane);
+      if (it + 1 < nt) load_v_dl(tnext(it, kb, 1), P ? Vd0 : Vd1);
       if (it < nt_w) {
         mask_max(kb, cur);
         qk(P ? Kd0 : Kd1, nxt);
