@@ -59,7 +59,12 @@ struct FwdCfg {
   static constexpr int NT = 64 * NW;            // threads per workgroup
   static constexpr int BR = 32 * NW * QS;       // query rows per workgroup
   static constexpr int BC = 64;                 // keys per tile
-  static constexpr int KSTR = D + 8;            // K tile row stride (elements)
+  // K tile row stride (elements). The tile is read by rows only (16-byte
+  // reads, 16 rows per LDS cycle): a 4-bank step keeps those conflict-free.
+  // The d=128 direct-to-LDS tile is unpadded and chunk-swizzled instead
+  // (tile_to_lds, swz), so each tile loads 16 KB, four blocks per wave.
+  static constexpr bool KSWZ = D == 128 && DL_;
+  static constexpr int KSTR = KSWZ ? D : D + 8;
   // V tile row stride: the 4 rows of a transposing read must land in
   // disjoint banks. At d=64 a stride of D+8 places them 36 banks apart (and
   // the smaller tile lets four workgroups share a CU). At d=128 the direct-
@@ -228,16 +233,22 @@ __global__ __launch_bounds__(C::NT, C::OCC * 4 / C::NW) void fwd_bf16_kernel(
   // S^T tiles from K tile Kt for every slab: rows = keys
   // 32*mt + (8i + 4g + j), column = the slab's query. Each K read serves
   // all QS slabs.
+  // This lane's K read offsets: chunk 2kk + g of row 32mt + r (the swizzle
+  // depends on r only, since 32mt leaves bits 0..3 of the row unchanged).
+  int k_off[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk)
+    k_off[kk] = C::KSWZ ? swz_off<D>(r, 16 * kk + 8 * g) : r * C::KSTR + 16 * kk + 8 * g;
   auto qk = [&](const u16* Kt, f32x16 (*sv)[BC / 32]) {
 #pragma unroll
     for (int mt = 0; mt < BC / 32; ++mt) {
-      const u16* kp = Kt + (32 * mt + r) * C::KSTR + 8 * g;
-      const bf16x8 a0 = ld_lds16(kp);
+      const u16* kp = Kt + 32 * mt * C::KSTR;
+      const bf16x8 a0 = ld_lds16(kp + k_off[0]);
 #pragma unroll
       for (int s = 0; s < QS; ++s) sv[s][mt] = mfma32_first(a0, qf[s][0]);
 #pragma unroll
       for (int kk = 1; kk < D / 16; ++kk) {
-        const bf16x8 a = ld_lds16(kp + 16 * kk);
+        const bf16x8 a = ld_lds16(kp + k_off[kk]);
 #pragma unroll
         for (int s = 0; s < QS; ++s) sv[s][mt] = mfma32(a, qf[s][kk], sv[s][mt]);
       }
@@ -349,7 +360,13 @@ __global__ __launch_bounds__(C::NT, C::OCC * 4 / C::NW) void fwd_bf16_kernel(
   };
 
   f32x16 s_cur[QS][BC / 32];
-  // Direct-to-LDS V tile load in the layout the reads above expect.
+  // Direct-to-LDS K and V tile loads in the layouts the reads above expect.
+  auto load_k_dl = [&](int kb, u16* Kt) {
+    if constexpr (C::KSWZ)
+      tile_to_lds<D, BC, C::NW>(rK, kb, Kt, w, lane);
+    else
+      tile_to_lds_padded<D, C::KSTR, BC, C::NW>(rK, kb, Kt, w, lane);
+  };
   auto load_v_dl = [&](int kb, u16* Vt) {
     if constexpr (C::VXOR)
       tile_to_lds_trxor<BC, C::NW>(rV, kb, Vt, w, lane);
@@ -362,10 +379,10 @@ __global__ __launch_bounds__(C::NT, C::OCC * 4 / C::NW) void fwd_bf16_kernel(
     // K_j left, V_{j+1} into the one V_{j-1} left. Two tiles per trip so
     // that the buffer names are compile-time constants.
     if (nt > 0) {
-      tile_to_lds_padded<D, C::KSTR, BC, C::NW>(rK, tnext(0, 0, 0), Kd0, w, lane);
+      load_k_dl(tnext(0, 0, 0), Kd0);
       load_v_dl(tnext(0, 0, 0), Vd0);
     }
-    if (nt > 1) tile_to_lds_padded<D, C::KSTR, BC, C::NW>(rK, tnext(0, 0, 1), Kd1, w, lane);
+    if (nt > 1) load_k_dl(tnext(0, 0, 1), Kd1);
     wait_vmem_all();
     __syncthreads();
     if (nt_w > 0) qk(Kd0, s_cur);
@@ -374,7 +391,7 @@ __global__ __launch_bounds__(C::NT, C::OCC * 4 / C::NW) void fwd_bf16_kernel(
     auto tile = [&](auto odd, int it, f32x16 (*cur)[BC / 32], f32x16 (*nxt)[BC / 32]) {
       constexpr bool P = decltype(odd)::value;
       const int kb = tnext(it, it * BC, 0);
-      if (it + 2 < nt) tile_to_lds_padded<D, C::KSTR, BC, C::NW>(rK, tnext(it, kb, 2), P ? Kd1 : Kd0, w, lane);
+      if (it + 2 < nt) load_k_dl(tnext(it, kb, 2), P ? Kd1 : Kd0);
       if (it + 1 < nt) load_v_dl(tnext(it, kb, 1), P ? Vd0 : Vd1);
       if (it < nt_w) {
         mask_max(kb, cur);
