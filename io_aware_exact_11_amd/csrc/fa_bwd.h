@@ -256,7 +256,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   __shared__ __attribute__((aligned(16))) u16 G0[BQ * QSTR];
   __shared__ __attribute__((aligned(16))) u16 G1[BQ * QSTR];
   __shared__ __attribute__((aligned(16))) float lse2s[2][BQ];
-  __shared__ __attribute__((aligned(16))) float Ds[2][BQ];
+  __shared__ __attribute__((aligned(16))) float Ds[2][BQ];  // -D_i
   // dQ path only: the workgroup's K rows (swizzled) and the dS tile(s).
   __shared__ __attribute__((aligned(16))) u16 Kt[DQ_ATOMIC ? C::BKV * D : 8];
   __shared__ __attribute__((aligned(16))) u16 dSs[DQ_ATOMIC ? NSPLIT * BQ * C::DSTR : 8];
@@ -330,9 +330,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     };
     auto store = [&](int buf) {
       if (tid < BQ) {
-        // rows past N: weight 0 (LSE = +inf) and no D term
+        // rows past N: weight 0 (LSE = +inf) and no D term. Stored as -D
+        // (dropout: -D / keep_scale), the start value of the dP product.
         lse2s[buf][tid] = qrow < N ? lraw * kLog2e : INFINITY;
-        Ds[buf][tid] = qrow < N ? draw : 0.f;
+        Ds[buf][tid] = qrow < N ? (DROP ? -draw / dpar.keep_scale : -draw) : 0.f;
       }
     };
     // Transposing-read coordinates of this lane (see ld_lds_tr): row part
@@ -370,7 +371,19 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
         for (int qt = 0; qt < BQ / 32; ++qt) {
           const int rb = 32 * qt * QSTR;
           sa[qt] = mfma32_first(ld_lds16(Qt + rb + rw0), kf[0]);
-          pa[qt] = mfma32_first(ld_lds16(Gt + rb + rw0), vf[0]);
+          {
+            // dP - D_i in one pass: the product accumulates onto -D_i of its
+            // row (element 4i + j is query 32qt + 8i + 4g + j); with dropout
+            // onto -D_i / keep_scale.
+            f32x16 nd;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const f32x4 d4 = *reinterpret_cast<const f32x4*>(&Ds[buf][32 * qt + 8 * i + 4 * g]);
+#pragma unroll
+              for (int j = 0; j < 4; ++j) nd[4 * i + j] = d4[j];
+            }
+            pa[qt] = mfma32(ld_lds16(Gt + rb + rw0), vf[0], nd);
+          }
 #pragma unroll
           for (int kk = 1; kk < D / 16; ++kk) {
             const int o = rb + 32 * (kk >> 1) + ((kk & 1) ? rw1 : rw0);
@@ -400,7 +413,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
           for (int i = 0; i < 4; ++i) {
             const int ql = 32 * qt + 8 * i + 4 * g;
             const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse2s[buf][ql]);
-            const f32x4 d4 = *reinterpret_cast<const f32x4*>(&Ds[buf][ql]);
+            f32x4 d4 = {};
+            if constexpr (DROP) d4 = *reinterpret_cast<const f32x4*>(&Ds[buf][ql]);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               const int e = 4 * i + j;
@@ -408,10 +422,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
               if constexpr (DROP) {
                 const bool keep = drop_keep(W, e, dpar.thresh);
                 sa[qt][e] = keep ? p : 0.f;
-                pa[qt][e] = p * ((keep ? pa[qt][e] * dpar.keep_scale : 0.f) - d4[j]);
+                // kept: p (ks dP - D); dropped: -p D (d4 holds -D / ks)
+                pa[qt][e] = (p * dpar.keep_scale) * (keep ? pa[qt][e] : d4[j]);
               } else {
                 sa[qt][e] = p;
-                pa[qt][e] = p * (pa[qt][e] - d4[j]);
+                pa[qt][e] = p * pa[qt][e];
               }
             }
           }

@@ -198,8 +198,13 @@ def test_forward_is_bitwise_reproducible_and_overwrites_outputs():
     assert torch.equal(g1[0], g2[0]) and torch.equal(g1[1], g2[1]) and torch.equal(g1[2], g2[2])
     g3 = fa.flash_attn_bwd(q, k, v, o, do, lse, causal=True, dq_atomic=True)
     torch.cuda.synchronize()
-    for a, c in zip(g3, g2):
-        assert torch.allclose(a, c, atol=1e-4, rtol=0)
+    # dK and dV come from the same key-outer arithmetic in both modes. dQ does
+    # not: each mode rounds dS to bf16 in a different kernel, from fp32 values
+    # formed in a different order, so single roundings may differ by one bf16
+    # ulp (2^-7 relative), moving dQ by up to 2^-7 |dS| |K| scale per flip.
+    # Both modes are checked against the oracle element by element elsewhere.
+    assert torch.allclose(g3[1], g2[1], atol=1e-4, rtol=0) and torch.allclose(g3[2], g2[2], atol=1e-4, rtol=0)
+    assert float((g3[0] - g2[0]).abs().max()) <= 1e-3 * max(1.0, float(g2[0].abs().max()))
 
 
 FULL = [
