@@ -261,13 +261,18 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   __shared__ __attribute__((aligned(16))) u16 Kt[DQ_ATOMIC ? C::BKV * D : 8];
   __shared__ __attribute__((aligned(16))) u16 dSs[DQ_ATOMIC ? NSPLIT * BQ * C::DSTR : 8];
 
+  // Causal grids pair key block i with block nkb - 1 - i in one workgroup,
+  // the one with more query rows (the lower) first, so that every workgroup
+  // does the same work.
+  const int per_head = causal ? (nkb + 1) / 2 : nkb;
   const int tile = xcd_tile(blockIdx.x, total);
-  const int kbi = tile % nkb;  // ascending: causal key blocks with the most rows first
-  const int bh = tile / nkb;
+  const int pi = tile % per_head;
+  const int bh = tile / per_head;
   const int b = bh / H;
-  const int kb0 = kbi * C::BKV;
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, r = lane & 31, g = lane >> 5;
+  auto block = [&](const int kbi) {
+  const int kb0 = kbi * C::BKV;
   const int kw0 = kb0 + 32 * w;
   const int key = kw0 + r;
   const size_t head = (size_t)bh * N * D;
@@ -539,6 +544,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
         *reinterpret_cast<f32x4*>(dvrow + 32 * t + 8 * i + 4 * g) = c;
       }
   }
+  };
+  block(pi);
+  if (causal && nkb - 1 - pi != pi) {
+    // The first block's waves are past their last barrier: no LDS reads of
+    // it remain.
+    __syncthreads();
+    block(nkb - 1 - pi);
+  }
 }
 
 template <int D>
@@ -586,12 +599,13 @@ __global__ __launch_bounds__(256, PRECISE ? 1 : 2) void bwd_dq_kernel(
   __shared__ __attribute__((aligned(16))) u16 V0[BC * VSTR];
   __shared__ __attribute__((aligned(16))) u16 V1[BC * VSTR];
 
+  // Causal grids pair query block i with block nqb - 1 - i in one
+  // workgroup, the longer first, so that every workgroup does the same work.
+  const int per_head = causal ? (nqb + 1) / 2 : nqb;
   const int tile = xcd_tile(blockIdx.x, total);
-  int qb = tile % nqb;
-  const int bh = tile / nqb;
-  if (causal) qb = nqb - 1 - qb;
+  const int pi = tile % per_head;
+  const int bh = tile / per_head;
   const int b = bh / H;
-  const int q0 = qb * C::BR;
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, r = lane & 31, g = lane >> 5;
   const size_t head = (size_t)bh * N * D;
@@ -606,6 +620,8 @@ __global__ __launch_bounds__(256, PRECISE ? 1 : 2) void bwd_dq_kernel(
     const int L = kv_len[b];
     kv_lim = L < 0 ? 0 : (L > N ? N : L);
   }
+  auto block = [&](const int qb) {
+  const int q0 = qb * C::BR;
   int kv_end = kv_lim;
   if (causal) kv_end = min(kv_end, q0 + C::BR);
   const int nt = (kv_end + BC - 1) / BC;
@@ -749,6 +765,14 @@ __global__ __launch_bounds__(256, PRECISE ? 1 : 2) void bwd_dq_kernel(
         *reinterpret_cast<f32x4*>(row + 32 * t + 8 * i + 4 * g) = a;
       }
   }
+  };
+  block(causal ? nqb - 1 - pi : pi);
+  if (causal && nqb - 1 - pi != pi) {
+    // The first block's waves are past their last barrier: no LDS reads of
+    // it remain.
+    __syncthreads();
+    block(pi);
+  }
 }
 
 template <int D, bool PRECISE, bool DQ_ATOMIC, bool DROP = false>
@@ -756,7 +780,7 @@ static void launch_dkdv(const u16* q, const u16* k, const u16* v, const u16* g, 
                         const float* Dws, float* dQ, float* dK, float* dV, const AttnShape& s, float sl2,
                         hipStream_t stream, DropParams dp = {}) {
   const int nkb = (s.N + DkdvCfg<D>::BKV - 1) / DkdvCfg<D>::BKV;
-  const int total = s.B * s.H * nkb;
+  const int total = s.B * s.H * (s.causal ? (nkb + 1) / 2 : nkb);
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, PRECISE, DQ_ATOMIC, DROP>), dim3(total), dim3(256), 0, stream, q, k, v,
                      g, LSE, Dws, dQ, dK, dV, s.H, s.N, s.scale, sl2, s.causal, s.kv_len, nkb, total, dp);
 }
@@ -766,7 +790,7 @@ static void launch_dq(const u16* q, const u16* k, const u16* v, const u16* o, co
                       const float* LSE, float* Dws, float* dQ, const AttnShape& s, float sl2,
                       hipStream_t stream, DropParams dp = {}) {
   const int nqb = (s.N + DqCfg<D>::BR - 1) / DqCfg<D>::BR;
-  const int total = s.B * s.H * nqb;
+  const int total = s.B * s.H * (s.causal ? (nqb + 1) / 2 : nqb);
   hipLaunchKernelGGL((bwd_dq_kernel<D, PRECISE, DROP>), dim3(total), dim3(256), 0, stream, q, k, v, o, g, LSE,
                      Dws, dQ, s.H, s.N, s.scale, sl2, s.causal, s.kv_len, nqb, total, dp);
 }

@@ -106,6 +106,12 @@ constexpr int kSparseMaxTiles = 1024;
 // per (query block, key block) of 128 x 128, row-major, bmask_stride bytes
 // apart for consecutive (b, h); only key tiles whose block is on are loaded
 // and computed, on top of the causal and padding masks.
+// Whether causal query blocks run in pairs (see fwd_bf16_kernel); not for
+// the dropout kernel at four waves per SIMD, whose 128 registers do not
+// hold the pairing's bookkeeping without spilling.
+template <class C, bool DROP>
+constexpr bool fwd_pairs() { return !(DROP && C::OCC >= 4); }
+
 template <int D, class C, bool DROP = false, bool SPARSE = false>
 __global__ __launch_bounds__(C::NT, C::OCC * 4 / C::NW) void fwd_bf16_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
@@ -126,12 +132,18 @@ __global__ __launch_bounds__(C::NT, C::OCC * 4 / C::NW) void fwd_bf16_kernel(
   __shared__ __attribute__((aligned(16))) u16 Vd0[DL ? BC * C::VSTR : 8];
   __shared__ __attribute__((aligned(16))) u16 Vd1[DL ? BC * C::VSTR : 8];
 
+  // Causal grids pair query block i with block nqb - 1 - i in one
+  // workgroup, run one after the other (the longer first): every workgroup
+  // then does the same amount of work, so no long block is left to start
+  // near the end of the grid, and both blocks read the same head's K and V.
+  // Unpaired causal grids run the longest blocks of each head first.
+  constexpr bool PAIR = fwd_pairs<C, DROP>();
+  const int per_head = (PAIR && causal) ? (nqb + 1) / 2 : nqb;
   const int tile = xcd_tile(blockIdx.x, total);
-  int qb = tile % nqb;
-  const int bh = tile / nqb;
-  if (causal) qb = nqb - 1 - qb;  // longest rows first
+  const int pi = tile % per_head;
+  const int bh = tile / per_head;
+  const int npass = (PAIR && causal && nqb - 1 - pi != pi) ? 2 : 1;
   const int b = bh / H;
-  const int q0 = qb * C::BR;
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, r = lane & 31, g = lane >> 5;
   const size_t head = (size_t)bh * N * D;
@@ -145,6 +157,9 @@ __global__ __launch_bounds__(C::NT, C::OCC * 4 / C::NW) void fwd_bf16_kernel(
     const int L = kv_len[b];
     kv_lim = L < 0 ? 0 : (L > N ? N : L);
   }
+
+  auto block = [&](const int qb) {
+  const int q0 = qb * C::BR;
   int kv_end = kv_lim;
   if (causal) kv_end = min(kv_end, q0 + C::BR);
   // Block-sparse: the ascending list of key tiles (64 keys, half a block)
@@ -500,6 +515,14 @@ __global__ __launch_bounds__(C::NT, C::OCC * 4 / C::NW) void fwd_bf16_kernel(
       if (g == 0) LSE[(size_t)bh * N + q] = l_tot > 0.f ? (m_run[s] + __log2f(l_tot)) * kLn2 : -INFINITY;
     }
   }
+  };
+  block(causal ? nqb - 1 - pi : pi);
+  if (npass == 2) {
+    // The first block's waves are past their last barrier (no LDS reads of
+    // it remain); the block-sparse tile list is rebuilt.
+    __syncthreads();
+    block(pi);
+  }
 }
 
 template <int D, class C, bool DROP = false, bool SPARSE = false>
@@ -507,7 +530,7 @@ static hipError_t launch_fwd_d(const void* Q, const void* K, const void* V, void
                                const AttnShape& s, hipStream_t stream, DropParams dp = {},
                                const uint8_t* bmask = nullptr, long long bmask_stride = 0) {
   const int nqb = (s.N + C::BR - 1) / C::BR;
-  const int total = s.B * s.H * nqb;
+  const int total = s.B * s.H * ((fwd_pairs<C, DROP>() && s.causal) ? (nqb + 1) / 2 : nqb);
   hipLaunchKernelGGL((fwd_bf16_kernel<D, C, DROP, SPARSE>), dim3(total), dim3(C::NT), 0, stream,
                      static_cast<const u16*>(Q), static_cast<const u16*>(K),
                      static_cast<const u16*>(V), static_cast<u16*>(O), LSE, s.H, s.N,
