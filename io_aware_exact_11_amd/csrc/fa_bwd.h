@@ -583,7 +583,7 @@ struct DqCfg {
 // dP of kept elements is scaled by the keep factor, dropped ones give
 // dS = -P D.
 template <int D, bool PRECISE, bool DROP = false>
-__global__ __launch_bounds__(256, PRECISE ? 1 : 2) void bwd_dq_kernel(
+__global__ __launch_bounds__(256, PRECISE ? 1 : (D == 64 && !DROP ? 3 : 2)) void bwd_dq_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
     const u16* __restrict__ O, const u16* __restrict__ dO, const float* __restrict__ LSE,
     float* __restrict__ Dg, float* __restrict__ dQ, int H, int N, float scale, float sl2, int causal,
