@@ -172,10 +172,20 @@ __global__ __launch_bounds__(C::NT, C::OCC * 4 / C::NW) void fwd_bf16_kernel(
   auto sparse_list = [&](int nt_all) {
     if (tid < 64) {
       const uint8_t* brow = bmask + (size_t)bh * bmask_stride + (size_t)qb * ((N + kSparseBlock - 1) / kSparseBlock);
+      // Every mask byte the list needs is requested before the first is
+      // used, so the row costs one memory latency rather than one per 64
+      // tiles. Indices are clamped into the row (a row has at least one
+      // block); tiles past nt_all are off.
+      constexpr int MAXIT = kSparseMaxTiles / 64;
+      const int tlast = nt_all > 0 ? nt_all - 1 : 0;
+      unsigned char mb[MAXIT];
+#pragma unroll
+      for (int i = 0; i < MAXIT; ++i) mb[i] = brow[min(64 * i + tid, tlast) >> 1];
       int cnt = 0;
-      for (int t0 = 0; t0 < nt_all; t0 += 64) {
-        const int t = t0 + tid;
-        const bool on = t < nt_all && brow[t >> 1] != 0;
+#pragma unroll
+      for (int i = 0; i < MAXIT; ++i) {
+        const int t = 64 * i + tid;
+        const bool on = t < nt_all && mb[i] != 0;
         const unsigned long long bal = __builtin_amdgcn_ballot_w64(on);
         const int pos = cnt + (int)__builtin_amdgcn_mbcnt_hi((unsigned)(bal >> 32),
                                                              __builtin_amdgcn_mbcnt_lo((unsigned)bal, 0u));
