@@ -220,7 +220,10 @@ template <int D>
 struct DkdvCfg {
   static constexpr int NW = 4;
   static constexpr int BKV = 32 * NW;          // keys per workgroup (32 per wave)
-  static constexpr int BQ = 64;                // query rows per block
+  // Query rows per block. At d=64 blocks of 32 rows keep the plain kernel
+  // within 168 VGPRs, i.e. three waves per SIMD (backward +3% at N=1024 and
+  // N=8192); at d=128 (one wave per SIMD) 32-row blocks measured 4% slower.
+  static constexpr int BQ = D == 64 ? 32 : 64;
   // Q and dO tile row stride (elements) of the xpad layout (xpad_off): both
   // tiles are read row-wise and transposed, conflict-free in that layout.
   static constexpr int QSTR = D + 32;
@@ -238,7 +241,7 @@ struct DkdvCfg {
 // dV takes the kept weights, dP of kept elements is scaled by the keep
 // factor and dropped ones contribute only the -P D term of dS.
 template <int D, bool PRECISE, bool DQ_ATOMIC, bool DROP = false>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(256, D == 64 && !PRECISE && !DQ_ATOMIC && !DROP ? 3 : 1) void bwd_dkdv_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
     const u16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dg,
     float* __restrict__ dQ, float* __restrict__ dK, float* __restrict__ dV, int H, int N, float scale,
