@@ -10,10 +10,11 @@
 // bandwidth-bound pre-pass computes from O and dO (default), or, with
 // FA_BWD_PRECISE, a separate recompute pass sums P o dP exactly.
 //
-// Main kernel (one workgroup per 128 keys of one (b, h), 4 waves of 32 keys):
+// Main kernel (one workgroup per 128 keys of one (b, h), two such key blocks
+// in causal grids, 4 waves of 32 keys):
 //   * the wave's K and V rows sit in registers as the B operands of
 //     S = Q K^T and dP = dO V^T (32x32x16 bf16 products, fp32 accumulate);
-//   * query blocks of 64 rows stream through LDS, stored both row-major
+//   * query blocks (64 rows at d=128, 32 at d=64) stream through LDS, stored both row-major
 //     (A operand of S and dP) and transposed (A operand of dV^T = dO^T P and
 //     dK^T = Q^T dS, whose B operands are the P and dS registers themselves);
 //   * dV^T and dK^T for the wave's keys accumulate in registers across all

@@ -1,11 +1,12 @@
 // Forward pass of exact attention for gfx950, bf16 in, fp32 accumulation.
 //
-// One workgroup owns BR query rows of one (b, h) (128, or 256 with two slabs
-// per wave) and streams the keys and values through LDS in tiles of BC = 64
-// rows, double-buffered: the global loads of the next tile are in flight
-// while the current one is computed ("FlashAttention and GPU Memory",
-// chapter 07 Blocks: one block of Q stays on chip while blocks of K and V
-// come in; only O and the row statistics are written back).
+// One workgroup owns a block of BR query rows of one (b, h) (128, or 256
+// with two slabs per wave; in causal grids two blocks, one after the other)
+// and streams the keys and values through LDS in tiles of BC = 64 rows,
+// double-buffered: the global loads of the next tile are in flight while
+// the current one is computed ("FlashAttention and GPU Memory", chapter 07
+// Blocks: one block of Q stays on chip while blocks of K and V come in;
+// only O and the row statistics are written back).
 //
 // Each of the 4 waves owns one or two 32-row query slabs. Scores are produced transposed,
 // S^T = K Q^T, with the 32x32x16 bf16 matrix-core product: A = a K tile
