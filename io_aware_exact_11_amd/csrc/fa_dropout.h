@@ -32,8 +32,9 @@ __device__ __forceinline__ u32x4 philox4x32_10(unsigned c0, unsigned c1, unsigne
   for (int round = 0; round < 10; ++round) {
     const unsigned long long p0 = (unsigned long long)c0 * 0xD2511F53u;
     const unsigned long long p1 = (unsigned long long)c2 * 0xCD9E8D57u;
-    const unsigned n0 = (unsigned)(p1 >> 32) ^ c1 ^ k0;
-    const unsigned n2 = (unsigned)(p0 >> 32) ^ c3 ^ k1;
+    // Three-input XORs, one v_bitop3_b32 each (truth table 0x96).
+    const unsigned n0 = __builtin_amdgcn_bitop3_b32((unsigned)(p1 >> 32), c1, k0, 0x96);
+    const unsigned n2 = __builtin_amdgcn_bitop3_b32((unsigned)(p0 >> 32), c3, k1, 0x96);
     c1 = (unsigned)p1;
     c3 = (unsigned)p0;
     c0 = n0;
