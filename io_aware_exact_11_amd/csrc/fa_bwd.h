@@ -276,278 +276,278 @@ __global__ __launch_bounds__(256, D == 64 && !PRECISE && !DQ_ATOMIC && !DROP ? 3
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, r = lane & 31, g = lane >> 5;
   auto block = [&](const int kbi) {
-  const int kb0 = kbi * C::BKV;
-  const int kw0 = kb0 + 32 * w;
-  const int key = kw0 + r;
-  const size_t head = (size_t)bh * N * D;
-  const unsigned head_bytes = (unsigned)N * D * 2;
+    const int kb0 = kbi * C::BKV;
+    const int kw0 = kb0 + 32 * w;
+    const int key = kw0 + r;
+    const size_t head = (size_t)bh * N * D;
+    const unsigned head_bytes = (unsigned)N * D * 2;
 
-  int kv_lim = N;
-  if (kv_len) {
-    const int L = kv_len[b];
-    kv_lim = L < 0 ? 0 : (L > N ? N : L);
-  }
-
-  f32x16 dv[D / 32], dk[D / 32];
-#pragma unroll
-  for (int t = 0; t < D / 32; ++t)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      dv[t][e] = 0.f;
-      dk[t][e] = 0.f;
+    int kv_lim = N;
+    if (kv_len) {
+      const int L = kv_len[b];
+      kv_lim = L < 0 ? 0 : (L > N ? N : L);
     }
 
-  if (kb0 < kv_lim) {
-    const auto rQ = make_rsrc(Q + head, head_bytes);
-    const auto rK = make_rsrc(K + head, head_bytes);
-    const auto rV = make_rsrc(V + head, head_bytes);
-    const auto rO = make_rsrc(dO + head, head_bytes);
-    bf16x8 kf[D / 16], vf[D / 16];
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      const unsigned off = (unsigned)(key * D + 16 * kk + 8 * g) * 2;
-      kf[kk] = as_bf16x8(ld_buf16(rK, off));
-      vf[kk] = as_bf16x8(ld_buf16(rV, off));
-    }
-    if constexpr (DQ_ATOMIC) {
-#pragma unroll
-      for (int rr = 0; rr < C::KCH; ++rr) {
-        const int c = tid + 256 * rr;
-        const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-        *reinterpret_cast<u32x4*>(&Kt[swz_off<D>(row, col)]) =
-            ld_buf16(rK, (unsigned)((kb0 + row) * D + col) * 2);
-      }
-    }
-
-    const int nqb = (N + BQ - 1) / BQ;
-    const int qb_start = causal ? kb0 / BQ : 0;
-    // Row statistics of the head through buffer resources: raw loads only
-    // here, arithmetic at store time, so that nothing waits on the prefetch
-    // (memory counters retire in order) until the block is written to LDS.
-    const auto rL = make_rsrc(LSE + (size_t)bh * N, (unsigned)N * 4);
-    const auto rD = make_rsrc(Dg + (size_t)bh * N, (unsigned)N * 4);
-    float lraw = 0.f, draw = 0.f;
-    int qrow = 0;
-    // Block q0: Q and dO rows straight into LDS; this thread's row
-    // statistics raw into registers (scaled when stored).
-    auto load = [&](int q0, u16* Qt, u16* Gt) {
-      tile_to_lds_xpad<D, QSTR, BQ, C::NW>(rQ, q0, Qt, w, lane);
-      tile_to_lds_xpad<D, QSTR, BQ, C::NW>(rO, q0, Gt, w, lane);
-      qrow = q0 + (tid & (BQ - 1));
-      lraw = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rL, (unsigned)qrow * 4, 0, 0));
-      draw = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rD, (unsigned)qrow * 4, 0, 0));
-    };
-    auto store = [&](int buf) {
-      if (tid < BQ) {
-        // rows past N: weight 0 (LSE = +inf) and no D term. Stored as -D
-        // (dropout: -D / keep_scale), the start value of the dP product.
-        lse2s[buf][tid] = qrow < N ? lraw * kLog2e : INFINITY;
-        Ds[buf][tid] = qrow < N ? (DROP ? -draw / dpar.keep_scale : -draw) : 0.f;
-      }
-    };
-    // Transposing-read coordinates of this lane (see ld_lds_tr): row part
-    // 4g + (lane % 16) / 4 inside a 16-row chunk, column part
-    // 16 * ((lane / 16) % 2) + 4 * (lane % 4) inside a 32-column tile.
-    const int tr_row = 4 * g + ((lane & 15) >> 2);
-    const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-    // This lane's offsets in the xpad tiles. Row-wise: chunk 2kk + g of row
-    // 32qt + r is at rw[kk % 2] + 32qt*QSTR + 32(kk / 2) (bits 2..3 of the row
-    // are those of r). Transposed: columns 32t + tr_col of rows
-    // 16c + tr_row + 8j are at tw[j] + 16c*QSTR + 32t (bits 2..3 of those
-    // rows are g + 2j).
-    const int xr = (r >> 2) & 3;
-    const int rw0 = r * QSTR + 8 * (g ^ xr), rw1 = r * QSTR + 8 * ((2 + g) ^ xr);
-    const int tw0 = tr_row * QSTR + 8 * ((tr_col >> 3) ^ g) + (tr_col & 7);
-    const int tw1 = (tr_row + 8) * QSTR + 8 * ((tr_col >> 3) ^ g ^ 2) + (tr_col & 7);
-
-    load(qb_start * BQ, Q0, G0);
-    wait_vmem_all();
-    store(0);
-    __syncthreads();
-    // Block qb: its tiles in buffer (qb - qb_start) % 2, the next block's
-    // loaded into the other meanwhile.
-    auto step = [&](auto odd, int qb) {
-      constexpr int buf = decltype(odd)::value ? 1 : 0;
-      const u16* Qt = buf ? Q1 : Q0;
-      const u16* Gt = buf ? G1 : G0;
-      const int q0 = qb * BQ;
-      if (qb + 1 < nqb) load(q0 + BQ, buf ? Q0 : Q1, buf ? G0 : G1);
-
-      if ((kw0 < kv_lim) && (!causal || q0 + BQ - 1 >= kw0)) {
-        // S = Q K^T, dP = dO V^T: rows = queries 32*qt + 8i + 4g + j, column = key.
-        f32x16 sa[BQ / 32], pa[BQ / 32];
-#pragma unroll
-        for (int qt = 0; qt < BQ / 32; ++qt) {
-          const int rb = 32 * qt * QSTR;
-          sa[qt] = mfma32_first(ld_lds16(Qt + rb + rw0), kf[0]);
-          {
-            // dP - D_i in one pass: the product accumulates onto -D_i of its
-            // row (element 4i + j is query 32qt + 8i + 4g + j); with dropout
-            // onto -D_i / keep_scale.
-            f32x16 nd;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const f32x4 d4 = *reinterpret_cast<const f32x4*>(&Ds[buf][32 * qt + 8 * i + 4 * g]);
-#pragma unroll
-              for (int j = 0; j < 4; ++j) nd[4 * i + j] = d4[j];
-            }
-            pa[qt] = mfma32(ld_lds16(Gt + rb + rw0), vf[0], nd);
-          }
-#pragma unroll
-          for (int kk = 1; kk < D / 16; ++kk) {
-            const int o = rb + 32 * (kk >> 1) + ((kk & 1) ? rw1 : rw0);
-            sa[qt] = mfma32(ld_lds16(Qt + o), kf[kk], sa[qt]);
-            pa[qt] = mfma32(ld_lds16(Gt + o), vf[kk], pa[qt]);
-          }
-        }
-        // Masked scores become -inf, so their weights come out exactly 0.
-        if ((kw0 + 31 >= kv_lim) || (causal && q0 < kw0 + 31)) {
-          // Element e of tile qt is query q0 + 4g + c with the constant
-          // c = 32qt + 8(e/4) + e%4; this lane's key is hidden from it iff the
-          // key is >= kv_lim (every c) or, causal, key > query (c < lim).
-          const int lim = key >= kv_lim ? INT_MAX : (causal ? key - q0 - 4 * g : INT_MIN);
-#pragma unroll
-          for (int qt = 0; qt < BQ / 32; ++qt)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-              const int c = 32 * qt + 8 * (e >> 2) + (e & 3);
-              sa[qt][e] = c < lim ? -INFINITY : sa[qt][e];
-            }
-        }
-#pragma unroll
-        for (int qt = 0; qt < BQ / 32; ++qt) {
-          unsigned W[4];
-          if constexpr (DROP) drop_words_key_lane(dpar, bh, key, q0 + 32 * qt, g, lane, W);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int ql = 32 * qt + 8 * i + 4 * g;
-            const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse2s[buf][ql]);
-            f32x4 d4 = {};
-            if constexpr (DROP) d4 = *reinterpret_cast<const f32x4*>(&Ds[buf][ql]);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const int e = 4 * i + j;
-              const float p = fast_exp2(sa[qt][e] * sl2 - l4[j]);
-              if constexpr (DROP) {
-                const bool keep = drop_keep(W, e, dpar.thresh);
-                sa[qt][e] = keep ? p : 0.f;
-                // kept: p (ks dP - D); dropped: -p D (d4 holds -D / ks)
-                pa[qt][e] = (p * dpar.keep_scale) * (keep ? pa[qt][e] : d4[j]);
-              } else {
-                sa[qt][e] = p;
-                pa[qt][e] = p * pa[qt][e];
-              }
-            }
-          }
-        }
-        bf16x8 pb[BQ / 16], db[BQ / 16], pl[PRECISE ? BQ / 16 : 1], dl[PRECISE ? BQ / 16 : 1];
-#pragma unroll
-        for (int c = 0; c < BQ / 16; ++c) {
-          if constexpr (PRECISE) {
-            pack_split_bf16x8(sa[c >> 1], 8 * (c & 1), pb[c], pl[c]);
-            pack_split_bf16x8(pa[c >> 1], 8 * (c & 1), db[c], dl[c]);
-          } else {
-            pb[c] = pack_bf16x8(sa[c >> 1], 8 * (c & 1));
-            db[c] = pack_bf16x8(pa[c >> 1], 8 * (c & 1));
-          }
-        }
-        // dV^T += dO^T P and dK^T += Q^T dS: A = the transposed tile (rows d =
-        // 32t + r, k-slots = queries 16c + 8h + 4g + 0..3 for slots 4h..4h+3),
-        // B = P / dS registers in the same slot order.
-#pragma unroll
-        for (int t = 0; t < D / 32; ++t)
-#pragma unroll
-          for (int c = 0; c < BQ / 16; ++c) {
-            const int o = 16 * c * QSTR + 32 * t;
-            const bf16x8 aO = join_tr(ld_lds_tr(Gt + o + tw0), ld_lds_tr(Gt + o + tw1));
-            const bf16x8 aQ = join_tr(ld_lds_tr(Qt + o + tw0), ld_lds_tr(Qt + o + tw1));
-            dv[t] = mfma32(aO, pb[c], dv[t]);
-            dk[t] = mfma32(aQ, db[c], dk[t]);
-            if constexpr (PRECISE) {
-              dv[t] = mfma32(aO, pl[c], dv[t]);
-              dk[t] = mfma32(aQ, dl[c], dk[t]);
-            }
-          }
-        if constexpr (DQ_ATOMIC) {
-          // dS (bf16, and its low half in precise mode) into the [query][key]
-          // tile: slot s of chunk c is query 16c + 8(s/4) + 4g + s%4.
-#pragma unroll
-          for (int part = 0; part < NSPLIT; ++part) {
-            u16* dst = dSs + part * BQ * C::DSTR;
-#pragma unroll
-            for (int c = 0; c < BQ / 16; ++c) {
-              const u32x4 words = __builtin_bit_cast(u32x4, part == 0 ? db[c] : dl[PRECISE ? c : 0]);
-#pragma unroll
-              for (int s8 = 0; s8 < 8; ++s8) {
-                const int ql = 16 * c + 8 * (s8 >> 2) + 4 * g + (s8 & 3);
-                dst[ql * C::DSTR + 32 * w + r] = (u16)(words[s8 >> 1] >> ((s8 & 1) * 16));
-              }
-            }
-          }
-        }
-      } else if constexpr (DQ_ATOMIC) {
-        for (int idx = lane; idx < NSPLIT * BQ * 4; idx += 64) {
-          const u32x4 z = {0u, 0u, 0u, 0u};
-          *reinterpret_cast<u32x4*>(&dSs[(idx >> 2) * C::DSTR + 32 * w + 8 * (idx & 3)]) = z;
-        }
-      }
-
-      if constexpr (DQ_ATOMIC) {
-        __syncthreads();
-        // dQ_i += s dS K over the workgroup's keys: 32x32 tiles (qt, dt) split
-        // over the waves; A = dS rows, B = K^T read transposed from Kt with
-        // the natural key order (k-slots 16c + 8g + 0..7).
-        constexpr int NT = (BQ / 32) * (D / 32);
-        const int kt_row = 8 * g + ((lane & 15) >> 2);
-        for (int tt = w; tt < NT; tt += C::NW) {
-          const int qt = tt / (D / 32), dt = tt % (D / 32);
-          f32x16 acc;
-#pragma unroll
-          for (int e = 0; e < 16; ++e) acc[e] = 0.f;
-#pragma unroll
-          for (int c = 0; c < C::BKV / 16; ++c) {
-            const int r0 = 16 * c + kt_row, col = 32 * dt + tr_col;
-            const bf16x8 bK = join_tr(ld_lds_tr(&Kt[swz_off<D>(r0, col)]),
-                                      ld_lds_tr(&Kt[swz_off<D>(r0 + 4, col)]));
-#pragma unroll
-            for (int part = 0; part < NSPLIT; ++part)
-              acc = mfma32(ld_lds16(&dSs[(part * BQ + 32 * qt + r) * C::DSTR + 16 * c + 8 * g]), bK, acc);
-          }
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int qq = q0 + 32 * qt + 8 * (e >> 2) + 4 * g + (e & 3);
-            if (qq < N) unsafeAtomicAdd(dQ + head + (size_t)qq * D + 32 * dt + r, acc[e] * scale);
-          }
-        }
-      }
-      // Each wave waits for its own loads before the barrier publishes them.
-      wait_vmem_all();
-      if (qb + 1 < nqb) store(buf ^ 1);
-      __syncthreads();
-    };
-    for (int qb = qb_start; qb < nqb; qb += 2) {
-      step(std::integral_constant<bool, false>{}, qb);
-      if (qb + 1 < nqb) step(std::integral_constant<bool, true>{}, qb + 1);
-    }
-  }
-
-  if (key < N) {
-    float* dkrow = dK + head + (size_t)key * D;
-    float* dvrow = dV + head + (size_t)key * D;
-#pragma unroll
+    f32x16 dv[D / 32], dk[D / 32];
+  #pragma unroll
     for (int t = 0; t < D / 32; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f32x4 a, c;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          a[j] = dk[t][4 * i + j] * scale;
-          c[j] = DROP ? dv[t][4 * i + j] * dpar.keep_scale : dv[t][4 * i + j];
-        }
-        *reinterpret_cast<f32x4*>(dkrow + 32 * t + 8 * i + 4 * g) = a;
-        *reinterpret_cast<f32x4*>(dvrow + 32 * t + 8 * i + 4 * g) = c;
+  #pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        dv[t][e] = 0.f;
+        dk[t][e] = 0.f;
       }
-  }
+
+    if (kb0 < kv_lim) {
+      const auto rQ = make_rsrc(Q + head, head_bytes);
+      const auto rK = make_rsrc(K + head, head_bytes);
+      const auto rV = make_rsrc(V + head, head_bytes);
+      const auto rO = make_rsrc(dO + head, head_bytes);
+      bf16x8 kf[D / 16], vf[D / 16];
+  #pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        const unsigned off = (unsigned)(key * D + 16 * kk + 8 * g) * 2;
+        kf[kk] = as_bf16x8(ld_buf16(rK, off));
+        vf[kk] = as_bf16x8(ld_buf16(rV, off));
+      }
+      if constexpr (DQ_ATOMIC) {
+  #pragma unroll
+        for (int rr = 0; rr < C::KCH; ++rr) {
+          const int c = tid + 256 * rr;
+          const int row = c / (D / 8), col = (c % (D / 8)) * 8;
+          *reinterpret_cast<u32x4*>(&Kt[swz_off<D>(row, col)]) =
+              ld_buf16(rK, (unsigned)((kb0 + row) * D + col) * 2);
+        }
+      }
+
+      const int nqb = (N + BQ - 1) / BQ;
+      const int qb_start = causal ? kb0 / BQ : 0;
+      // Row statistics of the head through buffer resources: raw loads only
+      // here, arithmetic at store time, so that nothing waits on the prefetch
+      // (memory counters retire in order) until the block is written to LDS.
+      const auto rL = make_rsrc(LSE + (size_t)bh * N, (unsigned)N * 4);
+      const auto rD = make_rsrc(Dg + (size_t)bh * N, (unsigned)N * 4);
+      float lraw = 0.f, draw = 0.f;
+      int qrow = 0;
+      // Block q0: Q and dO rows straight into LDS; this thread's row
+      // statistics raw into registers (scaled when stored).
+      auto load = [&](int q0, u16* Qt, u16* Gt) {
+        tile_to_lds_xpad<D, QSTR, BQ, C::NW>(rQ, q0, Qt, w, lane);
+        tile_to_lds_xpad<D, QSTR, BQ, C::NW>(rO, q0, Gt, w, lane);
+        qrow = q0 + (tid & (BQ - 1));
+        lraw = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rL, (unsigned)qrow * 4, 0, 0));
+        draw = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rD, (unsigned)qrow * 4, 0, 0));
+      };
+      auto store = [&](int buf) {
+        if (tid < BQ) {
+          // rows past N: weight 0 (LSE = +inf) and no D term. Stored as -D
+          // (dropout: -D / keep_scale), the start value of the dP product.
+          lse2s[buf][tid] = qrow < N ? lraw * kLog2e : INFINITY;
+          Ds[buf][tid] = qrow < N ? (DROP ? -draw / dpar.keep_scale : -draw) : 0.f;
+        }
+      };
+      // Transposing-read coordinates of this lane (see ld_lds_tr): row part
+      // 4g + (lane % 16) / 4 inside a 16-row chunk, column part
+      // 16 * ((lane / 16) % 2) + 4 * (lane % 4) inside a 32-column tile.
+      const int tr_row = 4 * g + ((lane & 15) >> 2);
+      const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+      // This lane's offsets in the xpad tiles. Row-wise: chunk 2kk + g of row
+      // 32qt + r is at rw[kk % 2] + 32qt*QSTR + 32(kk / 2) (bits 2..3 of the row
+      // are those of r). Transposed: columns 32t + tr_col of rows
+      // 16c + tr_row + 8j are at tw[j] + 16c*QSTR + 32t (bits 2..3 of those
+      // rows are g + 2j).
+      const int xr = (r >> 2) & 3;
+      const int rw0 = r * QSTR + 8 * (g ^ xr), rw1 = r * QSTR + 8 * ((2 + g) ^ xr);
+      const int tw0 = tr_row * QSTR + 8 * ((tr_col >> 3) ^ g) + (tr_col & 7);
+      const int tw1 = (tr_row + 8) * QSTR + 8 * ((tr_col >> 3) ^ g ^ 2) + (tr_col & 7);
+
+      load(qb_start * BQ, Q0, G0);
+      wait_vmem_all();
+      store(0);
+      __syncthreads();
+      // Block qb: its tiles in buffer (qb - qb_start) % 2, the next block's
+      // loaded into the other meanwhile.
+      auto step = [&](auto odd, int qb) {
+        constexpr int buf = decltype(odd)::value ? 1 : 0;
+        const u16* Qt = buf ? Q1 : Q0;
+        const u16* Gt = buf ? G1 : G0;
+        const int q0 = qb * BQ;
+        if (qb + 1 < nqb) load(q0 + BQ, buf ? Q0 : Q1, buf ? G0 : G1);
+
+        if ((kw0 < kv_lim) && (!causal || q0 + BQ - 1 >= kw0)) {
+          // S = Q K^T, dP = dO V^T: rows = queries 32*qt + 8i + 4g + j, column = key.
+          f32x16 sa[BQ / 32], pa[BQ / 32];
+  #pragma unroll
+          for (int qt = 0; qt < BQ / 32; ++qt) {
+            const int rb = 32 * qt * QSTR;
+            sa[qt] = mfma32_first(ld_lds16(Qt + rb + rw0), kf[0]);
+            {
+              // dP - D_i in one pass: the product accumulates onto -D_i of its
+              // row (element 4i + j is query 32qt + 8i + 4g + j); with dropout
+              // onto -D_i / keep_scale.
+              f32x16 nd;
+  #pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const f32x4 d4 = *reinterpret_cast<const f32x4*>(&Ds[buf][32 * qt + 8 * i + 4 * g]);
+  #pragma unroll
+                for (int j = 0; j < 4; ++j) nd[4 * i + j] = d4[j];
+              }
+              pa[qt] = mfma32(ld_lds16(Gt + rb + rw0), vf[0], nd);
+            }
+  #pragma unroll
+            for (int kk = 1; kk < D / 16; ++kk) {
+              const int o = rb + 32 * (kk >> 1) + ((kk & 1) ? rw1 : rw0);
+              sa[qt] = mfma32(ld_lds16(Qt + o), kf[kk], sa[qt]);
+              pa[qt] = mfma32(ld_lds16(Gt + o), vf[kk], pa[qt]);
+            }
+          }
+          // Masked scores become -inf, so their weights come out exactly 0.
+          if ((kw0 + 31 >= kv_lim) || (causal && q0 < kw0 + 31)) {
+            // Element e of tile qt is query q0 + 4g + c with the constant
+            // c = 32qt + 8(e/4) + e%4; this lane's key is hidden from it iff the
+            // key is >= kv_lim (every c) or, causal, key > query (c < lim).
+            const int lim = key >= kv_lim ? INT_MAX : (causal ? key - q0 - 4 * g : INT_MIN);
+  #pragma unroll
+            for (int qt = 0; qt < BQ / 32; ++qt)
+  #pragma unroll
+              for (int e = 0; e < 16; ++e) {
+                const int c = 32 * qt + 8 * (e >> 2) + (e & 3);
+                sa[qt][e] = c < lim ? -INFINITY : sa[qt][e];
+              }
+          }
+  #pragma unroll
+          for (int qt = 0; qt < BQ / 32; ++qt) {
+            unsigned W[4];
+            if constexpr (DROP) drop_words_key_lane(dpar, bh, key, q0 + 32 * qt, g, lane, W);
+  #pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int ql = 32 * qt + 8 * i + 4 * g;
+              const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse2s[buf][ql]);
+              f32x4 d4 = {};
+              if constexpr (DROP) d4 = *reinterpret_cast<const f32x4*>(&Ds[buf][ql]);
+  #pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const int e = 4 * i + j;
+                const float p = fast_exp2(sa[qt][e] * sl2 - l4[j]);
+                if constexpr (DROP) {
+                  const bool keep = drop_keep(W, e, dpar.thresh);
+                  sa[qt][e] = keep ? p : 0.f;
+                  // kept: p (ks dP - D); dropped: -p D (d4 holds -D / ks)
+                  pa[qt][e] = (p * dpar.keep_scale) * (keep ? pa[qt][e] : d4[j]);
+                } else {
+                  sa[qt][e] = p;
+                  pa[qt][e] = p * pa[qt][e];
+                }
+              }
+            }
+          }
+          bf16x8 pb[BQ / 16], db[BQ / 16], pl[PRECISE ? BQ / 16 : 1], dl[PRECISE ? BQ / 16 : 1];
+  #pragma unroll
+          for (int c = 0; c < BQ / 16; ++c) {
+            if constexpr (PRECISE) {
+              pack_split_bf16x8(sa[c >> 1], 8 * (c & 1), pb[c], pl[c]);
+              pack_split_bf16x8(pa[c >> 1], 8 * (c & 1), db[c], dl[c]);
+            } else {
+              pb[c] = pack_bf16x8(sa[c >> 1], 8 * (c & 1));
+              db[c] = pack_bf16x8(pa[c >> 1], 8 * (c & 1));
+            }
+          }
+          // dV^T += dO^T P and dK^T += Q^T dS: A = the transposed tile (rows d =
+          // 32t + r, k-slots = queries 16c + 8h + 4g + 0..3 for slots 4h..4h+3),
+          // B = P / dS registers in the same slot order.
+  #pragma unroll
+          for (int t = 0; t < D / 32; ++t)
+  #pragma unroll
+            for (int c = 0; c < BQ / 16; ++c) {
+              const int o = 16 * c * QSTR + 32 * t;
+              const bf16x8 aO = join_tr(ld_lds_tr(Gt + o + tw0), ld_lds_tr(Gt + o + tw1));
+              const bf16x8 aQ = join_tr(ld_lds_tr(Qt + o + tw0), ld_lds_tr(Qt + o + tw1));
+              dv[t] = mfma32(aO, pb[c], dv[t]);
+              dk[t] = mfma32(aQ, db[c], dk[t]);
+              if constexpr (PRECISE) {
+                dv[t] = mfma32(aO, pl[c], dv[t]);
+                dk[t] = mfma32(aQ, dl[c], dk[t]);
+              }
+            }
+          if constexpr (DQ_ATOMIC) {
+            // dS (bf16, and its low half in precise mode) into the [query][key]
+            // tile: slot s of chunk c is query 16c + 8(s/4) + 4g + s%4.
+  #pragma unroll
+            for (int part = 0; part < NSPLIT; ++part) {
+              u16* dst = dSs + part * BQ * C::DSTR;
+  #pragma unroll
+              for (int c = 0; c < BQ / 16; ++c) {
+                const u32x4 words = __builtin_bit_cast(u32x4, part == 0 ? db[c] : dl[PRECISE ? c : 0]);
+  #pragma unroll
+                for (int s8 = 0; s8 < 8; ++s8) {
+                  const int ql = 16 * c + 8 * (s8 >> 2) + 4 * g + (s8 & 3);
+                  dst[ql * C::DSTR + 32 * w + r] = (u16)(words[s8 >> 1] >> ((s8 & 1) * 16));
+                }
+              }
+            }
+          }
+        } else if constexpr (DQ_ATOMIC) {
+          for (int idx = lane; idx < NSPLIT * BQ * 4; idx += 64) {
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            *reinterpret_cast<u32x4*>(&dSs[(idx >> 2) * C::DSTR + 32 * w + 8 * (idx & 3)]) = z;
+          }
+        }
+
+        if constexpr (DQ_ATOMIC) {
+          __syncthreads();
+          // dQ_i += s dS K over the workgroup's keys: 32x32 tiles (qt, dt) split
+          // over the waves; A = dS rows, B = K^T read transposed from Kt with
+          // the natural key order (k-slots 16c + 8g + 0..7).
+          constexpr int NT = (BQ / 32) * (D / 32);
+          const int kt_row = 8 * g + ((lane & 15) >> 2);
+          for (int tt = w; tt < NT; tt += C::NW) {
+            const int qt = tt / (D / 32), dt = tt % (D / 32);
+            f32x16 acc;
+  #pragma unroll
+            for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+  #pragma unroll
+            for (int c = 0; c < C::BKV / 16; ++c) {
+              const int r0 = 16 * c + kt_row, col = 32 * dt + tr_col;
+              const bf16x8 bK = join_tr(ld_lds_tr(&Kt[swz_off<D>(r0, col)]),
+                                        ld_lds_tr(&Kt[swz_off<D>(r0 + 4, col)]));
+  #pragma unroll
+              for (int part = 0; part < NSPLIT; ++part)
+                acc = mfma32(ld_lds16(&dSs[(part * BQ + 32 * qt + r) * C::DSTR + 16 * c + 8 * g]), bK, acc);
+            }
+  #pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const int qq = q0 + 32 * qt + 8 * (e >> 2) + 4 * g + (e & 3);
+              if (qq < N) unsafeAtomicAdd(dQ + head + (size_t)qq * D + 32 * dt + r, acc[e] * scale);
+            }
+          }
+        }
+        // Each wave waits for its own loads before the barrier publishes them.
+        wait_vmem_all();
+        if (qb + 1 < nqb) store(buf ^ 1);
+        __syncthreads();
+      };
+      for (int qb = qb_start; qb < nqb; qb += 2) {
+        step(std::integral_constant<bool, false>{}, qb);
+        if (qb + 1 < nqb) step(std::integral_constant<bool, true>{}, qb + 1);
+      }
+    }
+
+    if (key < N) {
+      float* dkrow = dK + head + (size_t)key * D;
+      float* dvrow = dV + head + (size_t)key * D;
+  #pragma unroll
+      for (int t = 0; t < D / 32; ++t)
+  #pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          f32x4 a, c;
+  #pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            a[j] = dk[t][4 * i + j] * scale;
+            c[j] = DROP ? dv[t][4 * i + j] * dpar.keep_scale : dv[t][4 * i + j];
+          }
+          *reinterpret_cast<f32x4*>(dkrow + 32 * t + 8 * i + 4 * g) = a;
+          *reinterpret_cast<f32x4*>(dvrow + 32 * t + 8 * i + 4 * g) = c;
+        }
+    }
   };
   block(pi);
   if (causal && nkb - 1 - pi != pi) {
@@ -625,150 +625,150 @@ __global__ __launch_bounds__(256, PRECISE ? 1 : (D == 64 && !DROP ? 3 : 2)) void
     kv_lim = L < 0 ? 0 : (L > N ? N : L);
   }
   auto block = [&](const int qb) {
-  const int q0 = qb * C::BR;
-  int kv_end = kv_lim;
-  if (causal) kv_end = min(kv_end, q0 + C::BR);
-  const int nt = (kv_end + BC - 1) / BC;
-  const int q = q0 + 32 * w + r;
-  const int wave_q_first = q0 + 32 * w, wave_q_last = wave_q_first + 31;
-  const int nt_w = causal ? min(nt, wave_q_last / BC + 1) : nt;
+    const int q0 = qb * C::BR;
+    int kv_end = kv_lim;
+    if (causal) kv_end = min(kv_end, q0 + C::BR);
+    const int nt = (kv_end + BC - 1) / BC;
+    const int q = q0 + 32 * w + r;
+    const int wave_q_first = q0 + 32 * w, wave_q_last = wave_q_first + 31;
+    const int nt_w = causal ? min(nt, wave_q_last / BC + 1) : nt;
 
-  bf16x8 qf[D / 16], df[D / 16];
-#pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) {
-    const unsigned off = (unsigned)(q * D + 16 * kk + 8 * g) * 2;
-    qf[kk] = as_bf16x8(ld_buf16(rQ, off));
-    df[kk] = as_bf16x8(ld_buf16(rO, off));
-  }
-  const float lse2 = q < N ? LSE[(size_t)bh * N + q] * kLog2e : INFINITY;
-  float Dq;
-  if constexpr (PRECISE) {
-    Dq = q < N ? Dg[(size_t)bh * N + q] : 0.f;
-  } else {
-    // This lane holds d-chunks 16kk + 8g .. +7 of the row's dO; its partner
-    // lane (lane ^ 32) holds the other half. Rows past N read zeros.
-    const auto rOut = make_rsrc(O + head, head_bytes);
-    float part = 0.f;
-#pragma unroll
+    bf16x8 qf[D / 16], df[D / 16];
+  #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-      const u32x4 ov = ld_buf16(rOut, (unsigned)(q * D + 16 * kk + 8 * g) * 2);
-      const u32x4 gv = __builtin_bit_cast(u32x4, df[kk]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        part += __uint_as_float(bf16_bits(ov, e) << 16) * __uint_as_float(bf16_bits(gv, e) << 16);
+      const unsigned off = (unsigned)(q * D + 16 * kk + 8 * g) * 2;
+      qf[kk] = as_bf16x8(ld_buf16(rQ, off));
+      df[kk] = as_bf16x8(ld_buf16(rO, off));
     }
-    Dq = pair_sum(part);
-    if (q < N && g == 0) Dg[(size_t)bh * N + q] = Dq;
-  }
-
-  f32x16 acc[D / 32];
-#pragma unroll
-  for (int t = 0; t < D / 32; ++t)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) acc[t][e] = 0.f;
-
-  auto load = [&](int kb, u16* Kt, u16* Vt) {
-    tile_to_lds_xpad<D, KSTR, BC, C::NW>(rK, kb, Kt, w, lane);
-    tile_to_lds_padded<D, VSTR, BC, C::NW>(rV, kb, Vt, w, lane);
-  };
-  const int tr_row = 4 * g + ((lane & 15) >> 2);
-  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  // This lane's offsets in the xpad K tile, as in the dK/dV kernel: row-wise
-  // chunk 2kk + g of row 32mt + r at rw[kk % 2] + 32mt*KSTR + 32(kk / 2);
-  // transposed columns 32t + tr_col of rows 16c + tr_row + 8j at
-  // tw[j] + 16c*KSTR + 32t.
-  const int xr = (r >> 2) & 3;
-  const int rw0 = r * KSTR + 8 * (g ^ xr), rw1 = r * KSTR + 8 * ((2 + g) ^ xr);
-  const int tw0 = tr_row * KSTR + 8 * ((tr_col >> 3) ^ g) + (tr_col & 7);
-  const int tw1 = (tr_row + 8) * KSTR + 8 * ((tr_col >> 3) ^ g ^ 2) + (tr_col & 7);
-
-  if (nt > 0) load(0, K0, V0);
-  wait_vmem_all();
-  __syncthreads();
-  // Tile it: K_it, V_it in buffer it % 2; tile it+1 is loaded into the other.
-  auto step = [&](auto odd, int it) {
-    constexpr bool P = decltype(odd)::value;
-    const u16* Kc = P ? K1 : K0;
-    const u16* Vc = P ? V1 : V0;
-    const int kb = it * BC;
-    if (it + 1 < nt) load(kb + BC, P ? K0 : K1, P ? V0 : V1);
-    if (it < nt_w) {
-      f32x16 s[BC / 32], dp[BC / 32];
-#pragma unroll
-      for (int mt = 0; mt < BC / 32; ++mt) {
-        const int row = 32 * mt + r;
-        s[mt] = mfma32_first(ld_lds16(Kc + 32 * mt * KSTR + rw0), qf[0]);
-        dp[mt] = mfma32_first(ld_lds16(Vc + row * VSTR + 8 * g), df[0]);
-#pragma unroll
-        for (int kk = 1; kk < D / 16; ++kk) {
-          s[mt] = mfma32(ld_lds16(Kc + 32 * mt * KSTR + 32 * (kk >> 1) + ((kk & 1) ? rw1 : rw0)), qf[kk], s[mt]);
-          dp[mt] = mfma32(ld_lds16(Vc + row * VSTR + 16 * kk + 8 * g), df[kk], dp[mt]);
-        }
+    const float lse2 = q < N ? LSE[(size_t)bh * N + q] * kLog2e : INFINITY;
+    float Dq;
+    if constexpr (PRECISE) {
+      Dq = q < N ? Dg[(size_t)bh * N + q] : 0.f;
+    } else {
+      // This lane holds d-chunks 16kk + 8g .. +7 of the row's dO; its partner
+      // lane (lane ^ 32) holds the other half. Rows past N read zeros.
+      const auto rOut = make_rsrc(O + head, head_bytes);
+      float part = 0.f;
+  #pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        const u32x4 ov = ld_buf16(rOut, (unsigned)(q * D + 16 * kk + 8 * g) * 2);
+        const u32x4 gv = __builtin_bit_cast(u32x4, df[kk]);
+  #pragma unroll
+        for (int e = 0; e < 8; ++e)
+          part += __uint_as_float(bf16_bits(ov, e) << 16) * __uint_as_float(bf16_bits(gv, e) << 16);
       }
-      if ((kb + BC > kv_lim) || (causal && kb + BC - 1 > wave_q_first)) {
-        // Key kb + 4g + c, c = 32mt + 8(e/4) + e%4, is hidden iff c > lim.
-        const int lim = min(kv_lim - 1, causal ? q : kv_lim - 1) - (kb + 4 * g);
-#pragma unroll
-        for (int mt = 0; mt < BC / 32; ++mt)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int c = 32 * mt + 8 * (e >> 2) + (e & 3);
-            s[mt][e] = c > lim ? -INFINITY : s[mt][e];
-          }
-      }
-#pragma unroll
-      for (int mt = 0; mt < BC / 32; ++mt) {
-        unsigned W[4];
-        if constexpr (DROP) drop_words_query_lane(dpar, bh, q, kb + 32 * mt, g, lane, W);
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float p = fast_exp2(s[mt][e] * sl2 - lse2);
-          if constexpr (DROP)
-            dp[mt][e] = p * ((drop_keep(W, e, dpar.thresh) ? dp[mt][e] * dpar.keep_scale : 0.f) - Dq);
-          else
-            dp[mt][e] = p * (dp[mt][e] - Dq);
-        }
-      }
-      bf16x8 db[BC / 16], dl[PRECISE ? BC / 16 : 1];
-#pragma unroll
-      for (int c = 0; c < BC / 16; ++c) {
-        if constexpr (PRECISE)
-          pack_split_bf16x8(dp[c >> 1], 8 * (c & 1), db[c], dl[c]);
-        else
-          db[c] = pack_bf16x8(dp[c >> 1], 8 * (c & 1));
-      }
-      // dQ^T += K^T dS^T: A = K^T rows d = 32t + r, k-slots = keys of chunk c.
-#pragma unroll
-      for (int t = 0; t < D / 32; ++t)
-#pragma unroll
-        for (int c = 0; c < BC / 16; ++c) {
-          const int o = 16 * c * KSTR + 32 * t;
-          const bf16x8 aK = join_tr(ld_lds_tr(Kc + o + tw0), ld_lds_tr(Kc + o + tw1));
-          acc[t] = mfma32(aK, db[c], acc[t]);
-          if constexpr (PRECISE) acc[t] = mfma32(aK, dl[c], acc[t]);
-        }
+      Dq = pair_sum(part);
+      if (q < N && g == 0) Dg[(size_t)bh * N + q] = Dq;
     }
-    // Each wave waits for its own loads before the barrier publishes them.
+
+    f32x16 acc[D / 32];
+  #pragma unroll
+    for (int t = 0; t < D / 32; ++t)
+  #pragma unroll
+      for (int e = 0; e < 16; ++e) acc[t][e] = 0.f;
+
+    auto load = [&](int kb, u16* Kt, u16* Vt) {
+      tile_to_lds_xpad<D, KSTR, BC, C::NW>(rK, kb, Kt, w, lane);
+      tile_to_lds_padded<D, VSTR, BC, C::NW>(rV, kb, Vt, w, lane);
+    };
+    const int tr_row = 4 * g + ((lane & 15) >> 2);
+    const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    // This lane's offsets in the xpad K tile, as in the dK/dV kernel: row-wise
+    // chunk 2kk + g of row 32mt + r at rw[kk % 2] + 32mt*KSTR + 32(kk / 2);
+    // transposed columns 32t + tr_col of rows 16c + tr_row + 8j at
+    // tw[j] + 16c*KSTR + 32t.
+    const int xr = (r >> 2) & 3;
+    const int rw0 = r * KSTR + 8 * (g ^ xr), rw1 = r * KSTR + 8 * ((2 + g) ^ xr);
+    const int tw0 = tr_row * KSTR + 8 * ((tr_col >> 3) ^ g) + (tr_col & 7);
+    const int tw1 = (tr_row + 8) * KSTR + 8 * ((tr_col >> 3) ^ g ^ 2) + (tr_col & 7);
+
+    if (nt > 0) load(0, K0, V0);
     wait_vmem_all();
     __syncthreads();
-  };
-  for (int it = 0; it < nt; it += 2) {
-    step(std::integral_constant<bool, false>{}, it);
-    if (it + 1 < nt) step(std::integral_constant<bool, true>{}, it + 1);
-  }
-
-  if (q < N) {
-    float* row = dQ + head + (size_t)q * D;
-#pragma unroll
-    for (int t = 0; t < D / 32; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f32x4 a;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) a[j] = acc[t][4 * i + j] * scale;
-        *reinterpret_cast<f32x4*>(row + 32 * t + 8 * i + 4 * g) = a;
+    // Tile it: K_it, V_it in buffer it % 2; tile it+1 is loaded into the other.
+    auto step = [&](auto odd, int it) {
+      constexpr bool P = decltype(odd)::value;
+      const u16* Kc = P ? K1 : K0;
+      const u16* Vc = P ? V1 : V0;
+      const int kb = it * BC;
+      if (it + 1 < nt) load(kb + BC, P ? K0 : K1, P ? V0 : V1);
+      if (it < nt_w) {
+        f32x16 s[BC / 32], dp[BC / 32];
+  #pragma unroll
+        for (int mt = 0; mt < BC / 32; ++mt) {
+          const int row = 32 * mt + r;
+          s[mt] = mfma32_first(ld_lds16(Kc + 32 * mt * KSTR + rw0), qf[0]);
+          dp[mt] = mfma32_first(ld_lds16(Vc + row * VSTR + 8 * g), df[0]);
+  #pragma unroll
+          for (int kk = 1; kk < D / 16; ++kk) {
+            s[mt] = mfma32(ld_lds16(Kc + 32 * mt * KSTR + 32 * (kk >> 1) + ((kk & 1) ? rw1 : rw0)), qf[kk], s[mt]);
+            dp[mt] = mfma32(ld_lds16(Vc + row * VSTR + 16 * kk + 8 * g), df[kk], dp[mt]);
+          }
+        }
+        if ((kb + BC > kv_lim) || (causal && kb + BC - 1 > wave_q_first)) {
+          // Key kb + 4g + c, c = 32mt + 8(e/4) + e%4, is hidden iff c > lim.
+          const int lim = min(kv_lim - 1, causal ? q : kv_lim - 1) - (kb + 4 * g);
+  #pragma unroll
+          for (int mt = 0; mt < BC / 32; ++mt)
+  #pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const int c = 32 * mt + 8 * (e >> 2) + (e & 3);
+              s[mt][e] = c > lim ? -INFINITY : s[mt][e];
+            }
+        }
+  #pragma unroll
+        for (int mt = 0; mt < BC / 32; ++mt) {
+          unsigned W[4];
+          if constexpr (DROP) drop_words_query_lane(dpar, bh, q, kb + 32 * mt, g, lane, W);
+  #pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const float p = fast_exp2(s[mt][e] * sl2 - lse2);
+            if constexpr (DROP)
+              dp[mt][e] = p * ((drop_keep(W, e, dpar.thresh) ? dp[mt][e] * dpar.keep_scale : 0.f) - Dq);
+            else
+              dp[mt][e] = p * (dp[mt][e] - Dq);
+          }
+        }
+        bf16x8 db[BC / 16], dl[PRECISE ? BC / 16 : 1];
+  #pragma unroll
+        for (int c = 0; c < BC / 16; ++c) {
+          if constexpr (PRECISE)
+            pack_split_bf16x8(dp[c >> 1], 8 * (c & 1), db[c], dl[c]);
+          else
+            db[c] = pack_bf16x8(dp[c >> 1], 8 * (c & 1));
+        }
+        // dQ^T += K^T dS^T: A = K^T rows d = 32t + r, k-slots = keys of chunk c.
+  #pragma unroll
+        for (int t = 0; t < D / 32; ++t)
+  #pragma unroll
+          for (int c = 0; c < BC / 16; ++c) {
+            const int o = 16 * c * KSTR + 32 * t;
+            const bf16x8 aK = join_tr(ld_lds_tr(Kc + o + tw0), ld_lds_tr(Kc + o + tw1));
+            acc[t] = mfma32(aK, db[c], acc[t]);
+            if constexpr (PRECISE) acc[t] = mfma32(aK, dl[c], acc[t]);
+          }
       }
-  }
+      // Each wave waits for its own loads before the barrier publishes them.
+      wait_vmem_all();
+      __syncthreads();
+    };
+    for (int it = 0; it < nt; it += 2) {
+      step(std::integral_constant<bool, false>{}, it);
+      if (it + 1 < nt) step(std::integral_constant<bool, true>{}, it + 1);
+    }
+
+    if (q < N) {
+      float* row = dQ + head + (size_t)q * D;
+  #pragma unroll
+      for (int t = 0; t < D / 32; ++t)
+  #pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          f32x4 a;
+  #pragma unroll
+          for (int j = 0; j < 4; ++j) a[j] = acc[t][4 * i + j] * scale;
+          *reinterpret_cast<f32x4*>(row + 32 * t + 8 * i + 4 * g) = a;
+        }
+    }
   };
   block(causal ? nqb - 1 - pi : pi);
   if (causal && nqb - 1 - pi != pi) {
