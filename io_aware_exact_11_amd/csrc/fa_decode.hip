@@ -2,9 +2,9 @@
 // n_k key/value slots, the first kv_len[b] of which hold keys. One new
 // query against a long cache reads every cached key and value once and does
 // little arithmetic per byte, so the pass is bound by memory bandwidth
-// ("FlashAttention — why it mattered": token-by-token decoding has one new
-// query at a time and is limited by reading the cache), and it runs on the
-// vector ALUs rather than the matrix cores.
+// (decoding is the bandwidth-bound regime: "FlashAttention — why it
+// mattered", closing note), and it runs on the vector ALUs rather than the
+// matrix cores.
 //
 // The keys are split into chunks of 512 processed by separate workgroups
 // (so that a short batch still fills the GPU); each chunk keeps a running

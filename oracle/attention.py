@@ -34,9 +34,9 @@ Memory", chapter 08) and ``blockwise_attention_row`` (tiles of keys with the
 output rescaled by e^(m_old - m_new), chapter 08, and "FlashAttention does
 more arithmetic to move less data", the four moves).
 
-Decoding ("FlashAttention — why it mattered", the closing note that
-token-by-token decoding has one new query at a time and is limited by
-reading the cached keys and values): ``decode_head_forward`` takes n_q new
+Decoding (the bandwidth-bound regime in which each generated token brings a
+single query row that must read the whole cache; "FlashAttention — why it
+mattered", closing note): ``decode_head_forward`` takes n_q new
 queries against a cache of n_k key slots of which the first kv_len hold
 keys. Reading (the pages do not define it): the queries are the last n_q
 positions of that sequence, so with causal masking query i sees keys
@@ -163,8 +163,9 @@ def forward_rows(q, k, v, rows, scale, causal=False, kv_len=None):
 def online_softmax(scores, block):
     """Running-tally softmax over one row, ``block`` scores at a time.
 
-    Keeps the largest score so far m and the sum of exponentials measured
-    from it, l; a block with its own maximum mb and sum lb updates them as
+    The tally is a pair (m, l): the running row maximum and the running
+    sum of e^(x - m) over the scores seen so far. A block with its own
+    maximum mb and sum lb updates them as
     m' = max(m, mb), l' = e^(m - m') l + e^(mb - m') lb
     ("FlashAttention and GPU Memory", chapter 08). Returns (m, l, weights)
     with weights_j = e^(x_j - m) / l from the final tally.
