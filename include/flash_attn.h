@@ -51,7 +51,8 @@ typedef enum {
   FA_OK = 0,
   FA_ERR_INVALID_ARG = 1,
   FA_ERR_UNSUPPORTED = 2,
-  FA_ERR_HIP = 3
+  FA_ERR_HIP = 3,
+  FA_ERR_SCRATCH_LIMIT = 4
 } fa_status;
 
 /* flash_attn_bwd flags. */
@@ -97,6 +98,24 @@ int flash_attn_bwd(const void* Q, const void* K, const void* V, const void* O,
                    void* workspace, size_t workspace_bytes,
                    int B, int H, int N, int d, float scale, int causal,
                    const int32_t* kv_len, unsigned flags, void* stream);
+
+/*
+ * Allocation-free backward, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc). Same arguments, kernels, results and flags as flash_attn_bwd,
+ * without the workspace: the per-row term D_i lives in a fixed 16 MiB device
+ * array inside the library (one per GPU, held until the process ends),
+ * whose address is looked up on the first call on each device. Nothing is
+ * allocated or freed by the call. B*H*N above 4194304 rows returns
+ * FA_ERR_SCRATCH_LIMIT and launches nothing. Every call on one GPU shares
+ * that GPU's array: calls that overlap in time on one GPU (e.g. on two
+ * streams without ordering between them) race and give wrong gradients.
+ * The array's contents on entry do not matter.
+ */
+int flash_attn_bwd_noalloc(const void* Q, const void* K, const void* V, const void* O,
+                           const void* dO, const float* LSE, float* dQ, float* dK, float* dV,
+                           int B, int H, int N, int d, float scale, int causal,
+                           const int32_t* kv_len, unsigned flags, void* stream);
 
 /* Workspace bytes flash_attn_bwd / flash_attn_bwd_f32 need (0 for bad sizes). */
 size_t flash_attn_bwd_workspace_bytes(int B, int H, int N, int d, unsigned flags);

@@ -16,11 +16,12 @@ import torch
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libflashattn.so")
 _lib = None
 
-FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP, FA_ERR_SCRATCH_LIMIT = 0, 1, 2, 3, 4
+NOALLOC_MAX_ROWS = 4 << 20  # B*H*N limit of flash_attn_bwd_noalloc
 FA_BWD_PRECISE = 1
 FA_BWD_DQ_ATOMIC = 2
 
-EXPORTED = ("flash_attn_fwd", "flash_attn_bwd", "flash_attn_bwd_workspace_bytes",
+EXPORTED = ("flash_attn_fwd", "flash_attn_bwd", "flash_attn_bwd_noalloc", "flash_attn_bwd_workspace_bytes",
             "flash_attn_fwd_f32", "flash_attn_bwd_f32", "flash_attn_decode_fwd",
             "flash_attn_decode_workspace_bytes", "flash_attn_fwd_dropout", "flash_attn_bwd_dropout",
             "flash_attn_dropout_mask", "flash_attn_fwd_block_sparse", "flash_attn_fwd_fp8",
@@ -54,6 +55,8 @@ def load_library():
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = ctypes.c_int
+    lib.flash_attn_bwd_noalloc.argtypes = bwd_args[:9] + bwd_args[11:]
+    lib.flash_attn_bwd_noalloc.restype = ctypes.c_int
     lib.flash_attn_bwd_workspace_bytes.argtypes = [i, i, i, i, u]
     lib.flash_attn_bwd_workspace_bytes.restype = sz
     lib.flash_attn_decode_fwd.argtypes = [p, p, p, p, p, p, sz, i, i, i, i, i, f, i, p, p]
@@ -185,6 +188,34 @@ def flash_attn_bwd(q, k, v, o, do, lse, causal=False, scale=None, kv_len=None, p
     flags = (FA_BWD_PRECISE if precise else 0) | (FA_BWD_DQ_ATOMIC if dq_atomic else 0)
     return _bwd("flash_attn_bwd", torch.bfloat16, q, k, v, o, do, lse, causal, scale, kv_len, flags,
                 dq, dk, dv, workspace)
+
+
+def flash_attn_bwd_noalloc(q, k, v, o, do, lse, causal=False, scale=None, kv_len=None, precise=False,
+                           dq_atomic=False, dq=None, dk=None, dv=None):
+    """bf16 backward without a workspace (the library's fixed scratch holds D_i): returns fp32 (dQ, dK, dV).
+    Outputs the caller does not pass are allocated here; pass dq, dk, dv to allocate nothing."""
+    lib = load_library()
+    _check("q", q, torch.bfloat16, q.shape)
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    for nm, t in (("k", k), ("v", v), ("o", o), ("do", do)):
+        _check(nm, t, torch.bfloat16, q.shape)
+    _check("lse", lse, torch.float32, (B, H, N))
+    f32 = dict(dtype=torch.float32, device=q.device)
+    dq = torch.empty(q.shape, **f32) if dq is None else dq
+    dk = torch.empty(q.shape, **f32) if dk is None else dk
+    dv = torch.empty(q.shape, **f32) if dv is None else dv
+    for nm, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check(nm, t, torch.float32, q.shape)
+    kv_len = _kv(kv_len, B, q.device)
+    flags = (FA_BWD_PRECISE if precise else 0) | (FA_BWD_DQ_ATOMIC if dq_atomic else 0)
+    st = lib.flash_attn_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk),
+                                    _ptr(dv), B, H, N, d, _scale(scale, d), int(bool(causal)), _ptr(kv_len),
+                                    int(flags), _stream())
+    if st != FA_OK:
+        raise FlashAttnError(st, "flash_attn_bwd_noalloc")
+    return dq, dk, dv
 
 
 def flash_attn_bwd_f32(q, k, v, o, do, lse, causal=False, scale=None, kv_len=None,

@@ -5,7 +5,36 @@
 // with atomics.
 #include "fa_bwd.h"
 
+#include <mutex>
+
 namespace fa {
+
+// Fixed scratch of the allocation-free backward: D_i for up to kNoAllocRows
+// rows. Each GPU holds its own copy at its own address; host code never
+// passes the array's name to a kernel (in host code it is only a stand-in),
+// only the device address that hipGetSymbolAddress reports for the current
+// device.
+static __device__ __align__(256) float scratch[kNoAllocRows];
+
+hipError_t noalloc_scratch(float** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices];
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = static_cast<float*>(addr[dev]);
+  return hipSuccess;
+}
 
 __global__ void fill_zero_kernel(float4* __restrict__ p, size_t n4) {
   const size_t stride = (size_t)gridDim.x * blockDim.x;

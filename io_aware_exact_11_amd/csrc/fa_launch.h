@@ -77,6 +77,13 @@ hipError_t launch_bwd_bf16(const void* Q, const void* K, const void* V, const vo
                            float* Dws, const AttnShape& s, bool precise, bool dq_atomic,
                            hipStream_t stream);
 
+// Allocation-free backward: the per-row term D_i of at most kNoAllocRows
+// rows lives in a fixed device array (16 MiB per GPU for the life of the
+// process). noalloc_scratch returns its address on the current device,
+// looked up once per device.
+constexpr size_t kNoAllocRows = size_t(4) << 20;
+hipError_t noalloc_scratch(float** ptr);
+
 // Decoding: Nq new queries per (b, h) against Nk cache slots.
 struct DecodeShape {
   int B, H, Nq, Nk, d;

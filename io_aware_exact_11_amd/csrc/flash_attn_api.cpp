@@ -69,16 +69,18 @@ int fwd_common(const void* Q, const void* K, const void* V, void* O, float* LSE,
   return check_ptrs(in, in_p, 3, out, out_p, 2);
 }
 
+// Backward checks. has_ws = false: the caller passes no workspace (the
+// allocation-free entry point), so only the tensors are checked.
 int bwd_common(const void* Q, const void* K, const void* V, const void* O, const void* dO,
                const float* LSE, float* dQ, float* dK, float* dV, void* ws, size_t ws_bytes, int B,
                int H, int N, int d, float scale, int causal, unsigned flags, unsigned allowed_flags,
-               size_t esize) {
+               size_t esize, bool has_ws = true) {
   int st = check_shape(B, H, N, d, scale);
   if (st != FA_OK) return st;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
   if (flags & ~allowed_flags) return FA_ERR_INVALID_ARG;
   const size_t need = workspace_bytes(B, H, N);
-  if (ws_bytes < need) return FA_ERR_INVALID_ARG;
+  if (has_ws && ws_bytes < need) return FA_ERR_INVALID_ARG;
   const size_t tbytes = (size_t)B * H * N * d * esize;
   const size_t gbytes = (size_t)B * H * N * d * sizeof(float);
   const size_t lbytes = (size_t)B * H * N * sizeof(float);
@@ -87,7 +89,7 @@ int bwd_common(const void* Q, const void* K, const void* V, const void* O, const
                       span(O, tbytes), span(dO, tbytes), span(LSE, lbytes)};
   const void* out_p[4] = {dQ, dK, dV, ws};
   const Span out[4] = {span(dQ, gbytes), span(dK, gbytes), span(dV, gbytes), span(ws, need)};
-  return check_ptrs(in, in_p, 6, out, out_p, 4);
+  return check_ptrs(in, in_p, 6, out, out_p, has_ws ? 4 : 3);
 }
 
 size_t decode_ws_bytes(int B, int H, int Nq, int Nk, int d) {
@@ -134,6 +136,21 @@ int flash_attn_bwd(const void* Q, const void* K, const void* V, const void* O, c
                                         s, (flags & FA_BWD_PRECISE) != 0,
                                         (flags & FA_BWD_DQ_ATOMIC) != 0,
                                         static_cast<hipStream_t>(stream)));
+}
+
+int flash_attn_bwd_noalloc(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                           const float* LSE, float* dQ, float* dK, float* dV, int B, int H, int N, int d,
+                           float scale, int causal, const int32_t* kv_len, unsigned flags, void* stream) {
+  const int st = bwd_common(Q, K, V, O, dO, LSE, dQ, dK, dV, nullptr, 0, B, H, N, d, scale, causal, flags,
+                            FA_BWD_PRECISE | FA_BWD_DQ_ATOMIC, 2, false);
+  if (st != FA_OK) return st;
+  if ((size_t)B * H * N > fa::kNoAllocRows) return FA_ERR_SCRATCH_LIMIT;
+  float* scratch = nullptr;
+  const hipError_t e = fa::noalloc_scratch(&scratch);
+  if (e != hipSuccess) return FA_ERR_HIP;
+  const fa::AttnShape s{B, H, N, d, scale, causal, kv_len};
+  return hip_status(fa::launch_bwd_bf16(Q, K, V, O, dO, LSE, dQ, dK, dV, scratch, s, (flags & FA_BWD_PRECISE) != 0,
+                                        (flags & FA_BWD_DQ_ATOMIC) != 0, static_cast<hipStream_t>(stream)));
 }
 
 size_t flash_attn_bwd_workspace_bytes(int B, int H, int N, int d, unsigned flags) {
@@ -283,6 +300,8 @@ const char* flash_attn_status_string(int status) {
     case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG: an argument failed the host-side checks";
     case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: request is well-formed but not implemented";
     case FA_ERR_HIP: return "FA_ERR_HIP: a kernel launch failed";
+    case FA_ERR_SCRATCH_LIMIT:
+      return "FA_ERR_SCRATCH_LIMIT: B*H*N exceeds the 4194304 rows of the allocation-free entry point's fixed scratch";
     default: return "unknown flash_attn status";
   }
 }

@@ -36,8 +36,9 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for st in range(4):
-        assert fa.flash_attn_status_string(st).startswith(["FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_HIP"][st])
+    for st in range(5):
+        assert fa.flash_attn_status_string(st).startswith(
+            ["FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_HIP", "FA_ERR_SCRATCH_LIMIT"][st])
     assert "unknown" in fa.flash_attn_status_string(99)
 
 
@@ -108,6 +109,32 @@ def test_fwd_rejects(lib, fn, esize, kw, status):
 ])
 def test_bwd_rejects(lib, fn, kw, status):
     assert _bwd(lib, fn=fn, **kw) == status
+
+
+def _bwd_noalloc(lib, B=1, H=1, N=16, d=64, scale=0.125, causal=0, flags=0, ptrs=None):
+    step = (B * H * N * d * 4 + 4096 + 4095) // 4096 * 4096
+    base = [FAKE + i * step for i in range(9)]
+    if ptrs:
+        base = [ptrs.get(i, b) for i, b in enumerate(base)]
+    args = [ctypes.c_void_p(p) if p is not None else None for p in base]
+    return lib.flash_attn_bwd_noalloc(*args, B, H, N, d, scale, causal, None, flags, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), fa.binding.FA_ERR_INVALID_ARG),
+    (dict(d=80), fa.binding.FA_ERR_UNSUPPORTED),
+    (dict(scale=math.nan), fa.binding.FA_ERR_INVALID_ARG),
+    (dict(causal=5), fa.binding.FA_ERR_INVALID_ARG),
+    (dict(flags=1 << 5), fa.binding.FA_ERR_INVALID_ARG),
+    (dict(ptrs={5: None}), fa.binding.FA_ERR_INVALID_ARG),          # NULL LSE
+    (dict(ptrs={6: FAKE}), fa.binding.FA_ERR_INVALID_ARG),          # dQ aliases Q
+    (dict(ptrs={8: FAKE + 4}), fa.binding.FA_ERR_INVALID_ARG),      # misaligned dV
+    (dict(N=fa.binding.NOALLOC_MAX_ROWS + 1), fa.binding.FA_ERR_SCRATCH_LIMIT),
+    (dict(B=2, H=4, N=fa.binding.NOALLOC_MAX_ROWS // 8 + 1), fa.binding.FA_ERR_SCRATCH_LIMIT),
+])
+def test_bwd_noalloc_rejects(lib, kw, status):
+    # every case fails a host check before the scratch is looked up or anything is launched
+    assert _bwd_noalloc(lib, **kw) == status
 
 
 def test_f32_bwd_rejects_precise_flag(lib):
