@@ -137,8 +137,9 @@ int flash_attn_bwd_f32(const float* Q, const float* K, const float* V, const flo
 
 /*
  * Decoding forward, bf16: Nq new queries per (b, h) against a key/value
- * cache ("FlashAttention — why it mattered": token-by-token decoding has
- * one new query at a time and is limited by reading the cache).
+ * cache; each new token is a single query row that streams the whole cache,
+ * so the call is bound by memory bandwidth ("FlashAttention — why it
+ * mattered", closing note).
  *   Q:   bf16 [B,H,Nq,d], the new queries (1 <= Nq <= 8, Nq <= Nk);
  *   K,V: bf16 [B,H,Nk,d], the cache; slots j < kv_len[b] (all Nk when
  *        kv_len is NULL; values clamped to [0, Nk]) hold keys;
