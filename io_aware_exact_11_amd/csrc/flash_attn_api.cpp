@@ -6,6 +6,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <initializer_list>
+
 #include "fa_launch.h"
 
 namespace {
@@ -21,15 +23,30 @@ Span span(const void* p, size_t bytes) {
 
 bool overlaps(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
 
+// A range whose end passes the top of the address space cannot be a real
+// allocation; it would also defeat the overlap test.
+bool wraps(Span a) { return a.hi < a.lo; }
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Whether the product of positive int factors stays within int32 (the
+// kernels' element index range). Multiplied one factor at a time so that no
+// intermediate can overflow int64.
+bool fits_int32(std::initializer_list<int> factors) {
+  int64_t p = 1;
+  for (int f : factors) {
+    p *= f;  // p <= INT32_MAX and f <= INT32_MAX: no overflow
+    if (p > INT32_MAX) return false;
+  }
+  return true;
+}
 
 // Shape, scale and flag checks common to every entry point.
 int check_shape(int B, int H, int N, int d, float scale) {
   if (B < 1 || H < 1 || N < 1 || d < 1) return FA_ERR_INVALID_ARG;
   if (!isfinite(scale) || !(scale > 0.f)) return FA_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
-  const int64_t elems = (int64_t)B * H * N * d;
-  if (elems > INT32_MAX) return FA_ERR_UNSUPPORTED;
+  if (!fits_int32({B, H, N, d})) return FA_ERR_UNSUPPORTED;
   return FA_OK;
 }
 
@@ -38,9 +55,9 @@ int check_shape(int B, int H, int N, int d, float scale) {
 int check_ptrs(const Span* in, const void* const* in_p, int n_in, const Span* out,
                const void* const* out_p, int n_out) {
   for (int i = 0; i < n_in; ++i)
-    if (!in_p[i] || !aligned16(in_p[i])) return FA_ERR_INVALID_ARG;
+    if (!in_p[i] || !aligned16(in_p[i]) || wraps(in[i])) return FA_ERR_INVALID_ARG;
   for (int i = 0; i < n_out; ++i)
-    if (!out_p[i] || !aligned16(out_p[i])) return FA_ERR_INVALID_ARG;
+    if (!out_p[i] || !aligned16(out_p[i]) || wraps(out[i])) return FA_ERR_INVALID_ARG;
   for (int i = 0; i < n_out; ++i) {
     for (int j = 0; j < n_in; ++j)
       if (overlaps(out[i], in[j])) return FA_ERR_INVALID_ARG;
@@ -195,7 +212,7 @@ int flash_attn_decode_fwd(const void* Q, const void* K, const void* V, void* O, 
   if (Nq > Nk) return FA_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   if (Nq > 8) return FA_ERR_UNSUPPORTED;
-  if ((int64_t)B * H * Nk * d > INT32_MAX) return FA_ERR_UNSUPPORTED;
+  if (!fits_int32({B, H, Nk, d})) return FA_ERR_UNSUPPORTED;
   const size_t need = decode_ws_bytes(B, H, Nq, Nk, d);
   if (workspace_bytes_ < need) return FA_ERR_INVALID_ARG;
   const size_t qbytes = (size_t)B * H * Nq * d * 2;
@@ -252,6 +269,7 @@ int flash_attn_fwd_block_sparse(const void* Q, const void* K, const void* V, voi
   if (block_mask_head_stride > 0 && heads - 1 > (INT64_MAX - nb * nb) / block_mask_head_stride)
     return FA_ERR_INVALID_ARG;
   const Span mask = span(block_mask, (size_t)((heads - 1) * block_mask_head_stride + nb * nb));
+  if (wraps(mask)) return FA_ERR_INVALID_ARG;
   const size_t obytes = (size_t)B * H * N * d * 2, lbytes = (size_t)B * H * N * sizeof(float);
   if (overlaps(mask, span(O, obytes)) || overlaps(mask, span(LSE, lbytes))) return FA_ERR_INVALID_ARG;
   const fa::AttnShape s{B, H, N, d, scale, causal, kv_len};
