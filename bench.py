@@ -1,24 +1,29 @@
 """Benchmark: one step = exact-attention forward + backward over one batch.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME[:c|:nc]]
 
-Prints one JSON line. The step runs the library's whole path on inputs that
-are already resident in device memory: flash_attn_fwd (O, LSE) then
-flash_attn_bwd (query-outer dQ kernel, which also forms the row term D_i,
-then key-outer dK/dV kernel). FLOPs are
-counted over visible (query, key) pairs only: 4 d per pair forward (the two
-products S = Q K^T and O = P V at 2 flops per multiply-add) and 10 d per
-pair backward (recomputed S, dP, dV, dK, dQ), 14 d per pair for a step.
+Prints one JSON line. A step runs the library's whole path on inputs that
+are already resident in device memory: flash_attn_fwd (O, LSE), then
+flash_attn_bwd (the query-outer dQ kernel, which also forms the row term
+D_i, then the key-outer dK/dV kernel). FLOPs are algorithmic and counted
+over visible (query, key) pairs only: 4 d per pair forward (S = Q K^T and
+O = P V at 2 flops per multiply-add) and 10 d per pair backward (the
+recomputed S, dP, dV, dK, dQ), 14 d per pair for a step, whatever the mode
+executes on top of that.
 
-The primary workload is the GPT-2-medium attention shape (B=64, H=16,
-N=1024, d=64, causal); the N=4096 and N=16384 head-dim-128 workloads are
-timed the same way and reported under "workloads", next to the decoding
-forward (one new query per head against a 32K-slot cache), which is
-memory-bound and reported as an HBM rate, and the N=4096, d=128 workload
-again with fused dropout at p = 0.1 (same FLOP count; the generator work is
-not counted), the block-sparse forward on a 64K-long sequence (FLOPs
-over the visible pairs of its block mask), and the 8-bit (E4M3) forward on
-the N=4096, d=128 shape. Only one GPU is used.
+The headline workload is B=16, H=16, N=4096, d=128, non-causal: the target
+shapes are N >= 4096 at d=128, where the forward is to reach 50% and the
+forward + backward 35% of the MI355X dense bf16 matrix peak. The other
+step workloads (the same shape causal, the N=16384 causal long context, the
+GPT-2-medium attention shape and the padded batch with outlier keys) are
+timed the same way under "workloads", and "graded" lists the fractions of
+the target shapes next to their targets. Also under "workloads": the N=4096
+shape with fused dropout, the decoding forward (an HBM rate), the
+block-sparse forward on a 64K sequence and the 8-bit forward. Only one GPU
+is used.
+
+--only NAME (":c" causal, ":nc" non-causal) times that single step workload
+as the headline and nothing else (for per-workload profiles).
 """
 from __future__ import annotations
 
@@ -26,18 +31,30 @@ import argparse
 import hashlib
 import json
 import os
+import platform
 import sys
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 matrix-core peak (2.5 PFLOP/s class)
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 matrix-core peak (256 CUs x 4 SIMDs x 1024 flop/clk x 2.4 GHz)
 PEAK_HBM_TBPS = 8.0        # MI355X HBM3E peak
 PEAK_FP8_TFLOPS = 5000.0   # MI355X dense FP8 matrix-core peak
-PRIMARY = "gpt2_medium"
+FWD_TARGET, FWD_BWD_TARGET = 0.50, 0.35  # fractions of PEAK_BF16_TFLOPS at N >= 4096, d = 128
+PRIMARY = ("n4096_d128", False)
+GRADED = [("n4096_d128", False), ("n4096_d128", True), ("long_16k", True)]
+# (workload, causal, precise backward). The padded batch runs the precise
+# backward: its x8 outlier keys make gradients large enough that the
+# default mode misses the absolute error bar.
+STEP_WORKLOADS = [("n4096_d128", False, False), ("n4096_d128", True, False), ("long_16k", True, False),
+                  ("gpt2_medium", True, False), ("padded_8k", False, True)]
 DROPOUT_SEED = 0x5EED  # generator key of the dropout workload
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def case_key(name, causal):
+    return f"{name}:{'c' if causal else 'nc'}"
 
 
 def pairs_per_batch(w, causal, kv_len):
@@ -67,6 +84,18 @@ def kernel_source_digest():
         code = "\n".join(ln for ln in lines if ln)
         h.update(name.encode() + b"\0" + code.encode())
     return h.hexdigest()[:16]
+
+
+def stored_traffic(key):
+    """Counter bytes per call for workload key, if taken with the current device sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if tr.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    return tr.get("workloads", {}).get(key)
 
 
 class Case:
@@ -116,20 +145,24 @@ class Case:
                                dq=self.dq, dk=self.dk, dv=self.dv, workspace=self.ws)
 
     def run(self, steps, warmup):
-        """Time `steps` whole steps; per-kernel-call times from events on the stream."""
+        """Time exactly `steps` whole steps after `warmup` untimed ones. The
+        timed region is bracketed by device synchronisations; the forward and
+        backward calls are timed separately by HIP events recorded on the
+        stream the kernels are launched on."""
         import torch
         for _ in range(warmup):
             self.fwd()
             self.bwd()
-        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        torch.cuda.synchronize()
         t0 = time.perf_counter()
         for e in ev:
-            e[0].record()
+            e[0].record(stream)
             self.fwd()
-            e[1].record()
+            e[1].record(stream)
             self.bwd()
-            e[2].record()
+            e[2].record(stream)
         torch.cuda.synchronize()
         wall = (time.perf_counter() - t0) / steps
         fwd_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
@@ -137,37 +170,140 @@ class Case:
         return wall * 1e3, fwd_ms, bwd_ms
 
     def flops(self):
+        """Algorithmic forward and backward FLOPs of one step (4 d and 10 d per visible pair)."""
         d = self.w.d
-        mult_bwd = 14 if self.precise else 10  # precise: exact-D pass (2) and hi/lo products (2)
-        return 4 * d * self.pairs, mult_bwd * d * self.pairs
+        return 4 * d * self.pairs, 10 * d * self.pairs
+
+    def describe(self):
+        w = self.w
+        mask = "causal" if self.causal else ("key padding" if self.kv_host is not None else "non-causal")
+        mode = " (precise backward)" if self.precise else ""
+        drop = f" with dropout p={self.dropout}" if self.dropout else ""
+        return f"{self.name}: B={w.B} H={w.H} N={w.N} d={w.d} {mask}{drop}, fwd+bwd{mode}"
 
 
-def cpu_baseline(name, causal, budget_s=10.0):
-    """The fp64 oracle timed on this host's cores on a bounded sample of heads
-    of the same workload (its first heads in (b, h) order, until about
-    budget_s of work), reported in the same algorithmic TFLOP/s (14 d per pair)."""
+def measure(case, steps, warmup):
+    wms, fms, bms = case.run(steps, warmup)
+    ff, fb = case.flops()
+    fwd_t = ff / (fms * 1e-3) / 1e12
+    bwd_t = fb / (bms * 1e-3) / 1e12
+    step_t = (ff + fb) / (wms * 1e-3) / 1e12
+    w = case.w
+    return {"workload": case.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": case.causal,
+            "padded": case.kv_host is not None, "bwd_mode": "precise" if case.precise else "default",
+            **({"dropout": case.dropout} if case.dropout else {}),
+            "pairs": case.pairs, "ms_per_step": round(wms, 4), "fwd_ms": round(fms, 4), "bwd_ms": round(bms, 4),
+            "fwd_tflops": round(fwd_t, 2), "fwd_frac": round(fwd_t / PEAK_BF16_TFLOPS, 4),
+            "bwd_tflops": round(bwd_t, 2), "bwd_frac": round(bwd_t / PEAK_BF16_TFLOPS, 4),
+            "fwd_bwd_tflops": round(step_t, 2), "fwd_bwd_frac": round(step_t / PEAK_BF16_TFLOPS, 4)}
+
+
+def rooflines(case, res):
+    """Roofline objects: the backward call (the dominant cost: the dQ kernel
+    then the dK/dV kernel, one call timed by events) and the forward kernel."""
+    ff, fb = case.flops()
+    tr = stored_traffic(case_key(case.name, case.causal)) or {}
+    bwd_ach = fb / (res["bwd_ms"] * 1e-3) / 1e12
+    fwd_ach = ff / (res["fwd_ms"] * 1e-3) / 1e12
+    d = case.w.d
+    bwd = {"kernel": f"flash_attn_bwd call: bwd_dq_kernel<{d}> then bwd_dkdv_kernel<{d}>",
+           "bound": "mfma", "achieved": round(bwd_ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+           "frac": round(bwd_ach / PEAK_BF16_TFLOPS, 4), "traffic": tr.get("bwd_call_bytes"),
+           "algorithmic_flops_per_launch": fb, "avg_launch_ms": res["bwd_ms"]}
+    fwd = {"kernel": f"fwd_bf16_kernel<{d}>", "bound": "mfma", "achieved": round(fwd_ach, 2),
+           "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(fwd_ach / PEAK_BF16_TFLOPS, 4),
+           "traffic": tr.get("fwd_bytes"), "algorithmic_flops_per_launch": ff, "avg_launch_ms": res["fwd_ms"]}
+    return bwd, fwd
+
+
+def host_cpu():
+    model = platform.processor() or ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        nproc = len(os.sched_getaffinity(0))
+    except AttributeError:
+        nproc = os.cpu_count()
+    return model, nproc
+
+
+def cpu_oracle_sample(name, causal, fwd_budget_s, step_budget_s, min_heads=1):
+    """The fp64 oracle on this host over the first heads of a workload, in
+    (b, h) order: forward only until fwd_budget_s of work, then forward +
+    backward until step_budget_s (at least min_heads each). Throughput is in
+    the same algorithmic units as the GPU figures (4 d and 14 d per visible
+    pair of the heads timed); per-head seconds are scaled by the head count
+    to the whole workload."""
     import oracle
     from io_aware_exact_11_amd import workloads as wl
     w = wl.WORKLOADS[name]
+    x = wl.workload_inputs(name)
+    kv = x["kv_len"]
+    nh = w.B * w.H
+
+    def pairs(b):
+        if kv is not None:
+            L = max(0, min(int(kv[b]), w.N))
+            return sum(min(i + 1, L) for i in range(w.N)) if causal else w.N * L
+        return w.N * (w.N + 1) // 2 if causal else w.N * w.N
+
+    def timed(with_bwd, budget):
+        heads, prs, t0 = 0, 0, time.perf_counter()
+        while heads < nh and (heads < min_heads or time.perf_counter() - t0 < budget):
+            b, h = divmod(heads, w.H)
+            L = None if kv is None else int(kv[b])
+            oracle.head_forward(x["Q"][b, h], x["K"][b, h], x["V"][b, h], w.scale, causal, kv_len=L)
+            if with_bwd:
+                oracle.head_backward(x["Q"][b, h], x["K"][b, h], x["V"][b, h], x["dO"][b, h], w.scale, causal,
+                                     kv_len=L)
+            prs += pairs(b)
+            heads += 1
+        return heads, prs, time.perf_counter() - t0
+
+    hf, pf, tf = timed(False, fwd_budget_s)
+    hs, ps, ts = timed(True, step_budget_s)
+    del x
+    return {"workload": name, "causal": causal,
+            "fwd_tflops": 4 * w.d * pf / tf / 1e12, "fwd_heads": hf, "fwd_s_per_head": tf / hf,
+            "fwd_bwd_tflops": 14 * w.d * ps / ts / 1e12, "fwd_bwd_heads": hs, "fwd_bwd_s_per_head": ts / hs,
+            "whole_workload_fwd_s_scaled": tf / hf * nh, "whole_workload_fwd_bwd_s_scaled": ts / hs * nh,
+            "heads_total": nh}
+
+
+def cpu_baseline(primary, others):
+    """The fp64 oracle timed on this host's cores: a bounded sample of heads
+    of the headline workload (forward only, then forward + backward), and
+    one head of each other step workload."""
     try:
         from threadpoolctl import threadpool_info
         threads = max(i["num_threads"] for i in threadpool_info())
     except Exception:
         threads = os.cpu_count()
-    x = wl.workload_inputs(name)
-    heads, t0 = 0, time.perf_counter()
-    while heads < w.B * w.H and (time.perf_counter() - t0) < budget_s:
-        b, h = divmod(heads, w.H)
-        oracle.head_forward(x["Q"][b, h], x["K"][b, h], x["V"][b, h], w.scale, causal)
-        oracle.head_backward(x["Q"][b, h], x["K"][b, h], x["V"][b, h], x["dO"][b, h], w.scale, causal)
-        heads += 1
-    dt = time.perf_counter() - t0
-    per_head_pairs = w.N * (w.N + 1) // 2 if causal else w.N * w.N
-    tflops = 14 * w.d * per_head_pairs * heads / dt / 1e12
-    return {"value": tflops, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {heads} of {w.B * w.H} heads of {name} in (b, h) order, fwd+bwd "
-                      f"in float64 with numpy, {dt:.1f} s wall",
-            "seconds": round(dt, 2)}
+    model, nproc = host_cpu()
+    t0 = time.perf_counter()
+    main = cpu_oracle_sample(*primary, fwd_budget_s=4.0, step_budget_s=8.0)
+    per = [main]
+    for name, causal in others:
+        per.append(cpu_oracle_sample(name, causal, fwd_budget_s=0.0, step_budget_s=0.0))
+    total = time.perf_counter() - t0
+    for p in per:
+        for k in list(p):
+            if isinstance(p[k], float):
+                p[k] = round(p[k], 6)
+    return {"value": main["fwd_bwd_tflops"], "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": (f"{main['fwd_bwd_heads']} of {main['heads_total']} heads of {primary[0]} "
+                       f"({'causal' if primary[1] else 'non-causal'}) forward + backward and "
+                       f"{main['fwd_heads']} heads forward only, first heads in (b, h) order; one head forward "
+                       "and one forward + backward of each other step workload; numpy float64, algorithmic "
+                       "FLOPs over visible pairs"),
+            "fwd_value": main["fwd_tflops"], "nproc": nproc, "cpu_model": model,
+            "seconds_total": round(total, 1), "per_workload": per}
 
 
 def decode_case(steps, warmup):
@@ -190,12 +326,13 @@ def decode_case(steps, warmup):
     scale = float(d) ** -0.5
     for _ in range(warmup):
         fa.flash_attn_decode_fwd(q, k, v, causal=c["causal"], scale=scale, out=o, lse=lse, workspace=ws)
+    stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
+    e0.record(stream)
     for _ in range(steps):
         fa.flash_attn_decode_fwd(q, k, v, causal=c["causal"], scale=scale, out=o, lse=lse, workspace=ws)
-    e1.record()
+    e1.record(stream)
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / steps
     nbytes = 2 * B * H * Nk * d * 2 + 2 * B * H * Nq * d * 2 + B * H * Nq * 4
@@ -227,12 +364,13 @@ def block_sparse_case(steps, warmup):
     scale = float(d) ** -0.5
     for _ in range(warmup):
         fa.flash_attn_fwd_block_sparse(q, k, v, bm, causal=c["causal"], scale=scale, out=o, lse=lse)
+    stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
+    e0.record(stream)
     for _ in range(steps):
         fa.flash_attn_fwd_block_sparse(q, k, v, bm, causal=c["causal"], scale=scale, out=o, lse=lse)
-    e1.record()
+    e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
     # N is a multiple of 128 and the workload is non-causal: every on block is 128 x 128 visible pairs.
@@ -262,12 +400,13 @@ def fp8_case(steps, warmup):
     scale = float(d) ** -0.5
     for _ in range(warmup):
         fa.flash_attn_fwd_fp8(q8, k8, vt8, dq, dk, dv, causal=c["causal"], scale=scale, out=o, lse=lse)
+    stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
+    e0.record(stream)
     for _ in range(steps):
         fa.flash_attn_fwd_fp8(q8, k8, vt8, dq, dk, dv, causal=c["causal"], scale=scale, out=o, lse=lse)
-    e1.record()
+    e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
     pairs = B * H * (N * (N + 1) // 2 if c["causal"] else N * N)
@@ -300,13 +439,25 @@ def memory_sweep():
     return out
 
 
+def parse_only(spec):
+    name, _, mode = spec.partition(":")
+    from io_aware_exact_11_amd import workloads as wl
+    if name not in wl.WORKLOADS:
+        raise SystemExit(f"bench.py: unknown workload {name!r}; known: {sorted(wl.WORKLOADS)}")
+    for n, c, p in STEP_WORKLOADS:
+        if n == name and (mode == "" or c == (mode == "c")):
+            return n, c, p
+    raise SystemExit(f"bench.py: {spec!r} is not a step workload: {[case_key(n, c) for n, c, _ in STEP_WORKLOADS]}")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--only", default=None, help="time one step workload NAME[:c|:nc] only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extra", action="store_true", help="skip the N>=4096 workloads and the memory sweep")
+    ap.add_argument("--no-extra", action="store_true", help="headline workload only")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run one device-to-device copy of this many MiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -331,74 +482,79 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    case = Case(PRIMARY, causal=True)
-    wall_ms, fwd_ms, bwd_ms = case.run(args.steps, args.warmup)
-    ff, fb = case.flops()
-    value = (ff + fb) / (wall_ms * 1e-3) / 1e12
-    achieved = fb / (bwd_ms * 1e-3) / 1e12
+    if args.only:
+        head = parse_only(args.only)
+        extra_steps = []
+    else:
+        head = next(s for s in STEP_WORKLOADS if s[:2] == PRIMARY)
+        extra_steps = [] if args.no_extra else [s for s in STEP_WORKLOADS if s is not head]
 
-    traffic = None
-    try:
-        with open(TRAFFIC_FILE) as f:
-            tr = json.load(f)
-        if tr.get("kernel_source_digest") == kernel_source_digest() and tr.get("workload") == PRIMARY:
-            traffic = tr.get("bwd_call_bytes")
-    except (OSError, ValueError):
-        pass
+    print(f"bench: {case_key(*head[:2])} ({args.steps} steps)", file=sys.stderr, flush=True)
+    case = Case(head[0], head[1], precise=head[2])
+    res = measure(case, args.steps, args.warmup)
+    roof_bwd, roof_fwd = rooflines(case, res)
+    describe = case.describe()
+    del case
+    torch.cuda.empty_cache()
 
     result = {
         "metric": "attention fwd / fwd+bwd TFLOP/s (bf16) and % of MI355X MFMA peak, 1 GPU",
-        "value": round(value, 2),
+        "value": res["fwd_bwd_tflops"],
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(wall_ms, 4),
+        "ms_per_step": res["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "gpt2_medium: B=64 H=16 N=1024 d=64 causal, fwd+bwd",
-                   "B": case.w.B, "H": case.w.H, "N": case.w.N, "d": case.w.d, "causal": True,
-                   "parallelism": "none (1 GPU)"},
-        "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
-        "fwd_tflops": round(ff / (fwd_ms * 1e-3) / 1e12, 2),
-        "fwd_ms": round(fwd_ms, 4),
-        "bwd_ms": round(bwd_ms, 4),
-        "roofline": {"kernel": "flash_attn_bwd call (dQ kernel with the D_i row term + dK/dV kernel)",
-                     "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic},
+        "config": {"workload": describe, "B": res["B"], "H": res["H"], "N": res["N"], "d": res["d"],
+                   "causal": res["causal"], "bwd_mode": res["bwd_mode"], "parallelism": "none (1 GPU)"},
+        "frac_of_peak": res["fwd_bwd_frac"],
+        "fwd_tflops": res["fwd_tflops"], "fwd_frac": res["fwd_frac"], "fwd_ms": res["fwd_ms"],
+        "bwd_tflops": res["bwd_tflops"], "bwd_frac": res["bwd_frac"], "bwd_ms": res["bwd_ms"],
+        "roofline": roof_bwd,
+        "roofline_fwd": roof_fwd,
     }
-    del case
-    torch.cuda.empty_cache()
-
-    if not args.no_extra:
-        extra = []
-        for name, causal, drop in (("n4096_d128", False, None), ("n4096_d128", True, None), ("long_16k", True, None),
-                                   ("n4096_d128", False, 0.1)):
-            c = Case(name, causal, dropout=drop)
-            wms, fms, bms = c.run(args.steps, args.warmup)
-            cf, cb = c.flops()
-            extra.append({"workload": name, "causal": causal, **({"dropout": drop} if drop else {}),
-                          "ms_per_step": round(wms, 4),
-                          "fwd_tflops": round(cf / (fms * 1e-3) / 1e12, 2),
-                          "fwd_frac": round(cf / (fms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                          "fwd_bwd_tflops": round((cf + cb) / (wms * 1e-3) / 1e12, 2),
-                          "fwd_bwd_frac": round((cf + cb) / (wms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)})
-            del c
-            torch.cuda.empty_cache()
-        extra.append(decode_case(args.steps, args.warmup))
-        extra.append(block_sparse_case(args.steps, args.warmup))
+    steps_res = [res]
+    workloads = []
+    for name, causal, precise in extra_steps:
+        print(f"bench: {case_key(name, causal)}", file=sys.stderr, flush=True)
+        c = Case(name, causal, precise=precise)
+        r = measure(c, args.steps, args.warmup)
+        del c
         torch.cuda.empty_cache()
-        extra.append(fp8_case(args.steps, args.warmup))
+        workloads.append(r)
+        steps_res.append(r)
+    if extra_steps:
+        print("bench: dropout, decode, block-sparse, 8-bit, memory sweep", file=sys.stderr, flush=True)
+        c = Case("n4096_d128", False, dropout=0.1)
+        workloads.append(measure(c, args.steps, args.warmup))
+        del c
         torch.cuda.empty_cache()
-        result["workloads"] = extra
+        workloads.append(decode_case(args.steps, args.warmup))
+        workloads.append(block_sparse_case(args.steps, args.warmup))
+        torch.cuda.empty_cache()
+        workloads.append(fp8_case(args.steps, args.warmup))
+        torch.cuda.empty_cache()
+        result["workloads"] = workloads
         result["memory_sweep_B2_H16_d128_causal"] = memory_sweep()
+    graded = []
+    for r in steps_res:
+        if (r["workload"], r["causal"]) in GRADED and "dropout" not in r:
+            graded.append({"workload": case_key(r["workload"], r["causal"]),
+                           "fwd_frac": r["fwd_frac"], "fwd_target": FWD_TARGET,
+                           "fwd_met": r["fwd_frac"] >= FWD_TARGET,
+                           "fwd_bwd_frac": r["fwd_bwd_frac"], "fwd_bwd_target": FWD_BWD_TARGET,
+                           "fwd_bwd_met": r["fwd_bwd_frac"] >= FWD_BWD_TARGET})
+    result["graded"] = graded
 
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(PRIMARY, causal=True)
+    if not args.no_cpu_baseline and not args.only:
+        print("bench: cpu baseline (fp64 oracle on the host)", file=sys.stderr, flush=True)
+        others = [(n, c) for n, c, _ in STEP_WORKLOADS if (n, c) != PRIMARY]
+        result["cpu_baseline"] = cpu_baseline(PRIMARY, others)
     print(json.dumps(result), flush=True)
 
 
