@@ -241,14 +241,22 @@ struct DkdvCfg {
 // DROP: fused dropout regenerated from the generator state (fa_dropout.h):
 // dV takes the kept weights, dP of kept elements is scaled by the keep
 // factor and dropped ones contribute only the -P D term of dS.
+// The plain d=128 instance keeps V in LDS instead of registers and takes
+// query blocks of 32 rows: its registers then fit two waves per SIMD.
+template <int D, bool PRECISE, bool DQ_ATOMIC, bool DROP>
+constexpr bool dkdv_v_in_lds() { return D == 128 && !PRECISE && !DQ_ATOMIC && !DROP; }
+
 template <int D, bool PRECISE, bool DQ_ATOMIC, bool DROP = false>
-__global__ __launch_bounds__(256, D == 64 && !PRECISE && !DQ_ATOMIC && !DROP ? 3 : 1) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(256, D == 64 && !PRECISE && !DQ_ATOMIC && !DROP
+                                      ? 3
+                                      : (dkdv_v_in_lds<D, PRECISE, DQ_ATOMIC, DROP>() ? 2 : 1)) void bwd_dkdv_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
     const u16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dg,
     float* __restrict__ dQ, float* __restrict__ dK, float* __restrict__ dV, int H, int N, float scale,
     float sl2, int causal, const int32_t* __restrict__ kv_len, int nkb, int total, DropParams dpar) {
   using C = DkdvCfg<D>;
-  constexpr int BQ = C::BQ;
+  constexpr bool VLDS = dkdv_v_in_lds<D, PRECISE, DQ_ATOMIC, DROP>();
+  constexpr int BQ = VLDS ? 32 : C::BQ;
   constexpr int NSPLIT = PRECISE ? 2 : 1;
   constexpr int QSTR = C::QSTR;
   // Q and dO blocks arrive by direct-to-LDS loads into padded tiles. The two
@@ -264,6 +272,9 @@ __global__ __launch_bounds__(256, D == 64 && !PRECISE && !DQ_ATOMIC && !DROP ? 3
   // dQ path only: the workgroup's K rows (swizzled) and the dS tile(s).
   __shared__ __attribute__((aligned(16))) u16 Kt[DQ_ATOMIC ? C::BKV * D : 8];
   __shared__ __attribute__((aligned(16))) u16 dSs[DQ_ATOMIC ? NSPLIT * BQ * C::DSTR : 8];
+  // V rows of the workgroup's keys (swizzled, read by rows as the B operand
+  // of dP = dO V^T) when they are not held in registers.
+  __shared__ __attribute__((aligned(16))) u16 Vl[VLDS ? C::BKV * D : 8];
 
   // Causal grids pair key block i with block nkb - 1 - i in one workgroup,
   // the one with more query rows (the lower) first, so that every workgroup
@@ -302,13 +313,21 @@ __global__ __launch_bounds__(256, D == 64 && !PRECISE && !DQ_ATOMIC && !DROP ? 3
       const auto rK = make_rsrc(K + head, head_bytes);
       const auto rV = make_rsrc(V + head, head_bytes);
       const auto rO = make_rsrc(dO + head, head_bytes);
-      bf16x8 kf[D / 16], vf[D / 16];
+      bf16x8 kf[D / 16], vf[VLDS ? 1 : D / 16];
   #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
         const unsigned off = (unsigned)(key * D + 16 * kk + 8 * g) * 2;
         kf[kk] = as_bf16x8(ld_buf16(rK, off));
-        vf[kk] = as_bf16x8(ld_buf16(rV, off));
+        if constexpr (!VLDS) vf[kk] = as_bf16x8(ld_buf16(rV, off));
       }
+      if constexpr (VLDS) tile_to_lds<D, C::BKV, C::NW>(rV, kb0, Vl, w, lane);
+      // B operand of dP for d-chunk kk: this wave's key row 32w + r of Vl.
+      auto vop = [&](int kk) {
+        if constexpr (VLDS)
+          return ld_lds16(Vl + swz_off<D>(32 * w + r, 16 * kk + 8 * g));
+        else
+          return vf[kk];
+      };
       if constexpr (DQ_ATOMIC) {
   #pragma unroll
         for (int rr = 0; rr < C::KCH; ++rr) {
@@ -331,8 +350,18 @@ __global__ __launch_bounds__(256, D == 64 && !PRECISE && !DQ_ATOMIC && !DROP ? 3
       // Block q0: Q and dO rows straight into LDS; this thread's row
       // statistics raw into registers (scaled when stored).
       auto load = [&](int q0, u16* Qt, u16* Gt) {
-        tile_to_lds_xpad<D, QSTR, BQ, C::NW>(rQ, q0, Qt, w, lane);
-        tile_to_lds_xpad<D, QSTR, BQ, C::NW>(rO, q0, Gt, w, lane);
+        if constexpr (VLDS) {
+          // 32-row tiles are ten 1 KB blocks each: waves 0-1 fill the Q tile
+          // and waves 2-3 the dO tile, five blocks per wave.
+          const int ws = __builtin_amdgcn_readfirstlane(w);
+          if (ws < 2)
+            tile_to_lds_xpad<D, QSTR, BQ, 2>(rQ, q0, Qt, ws, lane);
+          else
+            tile_to_lds_xpad<D, QSTR, BQ, 2>(rO, q0, Gt, ws - 2, lane);
+        } else {
+          tile_to_lds_xpad<D, QSTR, BQ, C::NW>(rQ, q0, Qt, w, lane);
+          tile_to_lds_xpad<D, QSTR, BQ, C::NW>(rO, q0, Gt, w, lane);
+        }
         qrow = q0 + (tid & (BQ - 1));
         lraw = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rL, (unsigned)qrow * 4, 0, 0));
         draw = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rD, (unsigned)qrow * 4, 0, 0));
@@ -391,13 +420,13 @@ __global__ __launch_bounds__(256, D == 64 && !PRECISE && !DQ_ATOMIC && !DROP ? 3
   #pragma unroll
                 for (int j = 0; j < 4; ++j) nd[4 * i + j] = d4[j];
               }
-              pa[qt] = mfma32(ld_lds16(Gt + rb + rw0), vf[0], nd);
+              pa[qt] = mfma32(ld_lds16(Gt + rb + rw0), vop(0), nd);
             }
   #pragma unroll
             for (int kk = 1; kk < D / 16; ++kk) {
               const int o = rb + 32 * (kk >> 1) + ((kk & 1) ? rw1 : rw0);
               sa[qt] = mfma32(ld_lds16(Qt + o), kf[kk], sa[qt]);
-              pa[qt] = mfma32(ld_lds16(Gt + o), vf[kk], pa[qt]);
+              pa[qt] = mfma32(ld_lds16(Gt + o), vop(kk), pa[qt]);
             }
           }
           // Masked scores become -inf, so their weights come out exactly 0.

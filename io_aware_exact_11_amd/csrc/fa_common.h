@@ -17,6 +17,12 @@ typedef __attribute__((__vector_size__(2 * sizeof(unsigned)))) unsigned u32x2;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// Rescale threshold of the forward kernels, in base-2 units of the scaled
+// score: the running maximum only moves (and O, l are only rescaled) when a
+// tile's maximum exceeds it by more than this, so unnormalised weights stay
+// below 2^8.
+constexpr float kRescaleSlack = 8.f;
+
 // 32x32x16 bf16 matrix-core product with fp32 accumulation (wave64).
 // Operand layout, lane l = 32*g + r (g in {0,1}, r in 0..31):
 //   A (32 x 16): lane holds row r, k = 8g .. 8g+7

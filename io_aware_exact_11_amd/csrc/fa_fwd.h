@@ -90,10 +90,6 @@ using FwdCfg128 = FwdCfg<128, 4, 1, true, 2, true>;
 using FwdCfg64Causal = FwdCfg<64, 4, 1, false, 4>;
 using FwdCfg64Full = FwdCfg<64, 4, 2, false, 2>;
 
-// Rescale threshold, in base-2 units of the scaled score: the running
-// maximum only moves (and O, l are only rescaled) when a tile's maximum
-// exceeds it by more than this, so unnormalised weights stay below 2^8.
-constexpr float kRescaleSlack = 8.f;
 
 // Block-sparse attention: blocks of kSparseBlock queries by kSparseBlock keys,
 // at most kSparseMaxTiles key tiles (N <= 65536) per row of blocks.

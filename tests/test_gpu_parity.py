@@ -207,28 +207,100 @@ def test_forward_is_bitwise_reproducible_and_overwrites_outputs():
     assert float((g3[0] - g2[0]).abs().max()) <= 1e-3 * max(1.0, float(g2[0].abs().max()))
 
 
+def subset_heads(B, H, seed, n_random=4):
+    """The deterministic head subset checked at full size: first and last b,
+    h in {0, H-1}, plus n_random seeded (b, h) pairs."""
+    heads = {(b, h) for b in (0, B - 1) for h in (0, H - 1)}
+    rng = np.random.default_rng(seed)
+    while len(heads) < min(B * H, 4 + n_random):
+        heads.add((int(rng.integers(B)), int(rng.integers(H))))
+    return sorted(heads)
+
+
+# name, causal, precise, number of seeded heads beyond the corners (the
+# N=16384 heads take the oracle about 10 GB and ten seconds each: fewer)
 FULL = [
-    ("gpt2_medium", True, False, [(0, 0), (63, 15), (31, 7)]),
-    ("n4096_d128", False, False, [(0, 0), (15, 15)]),
-    ("n4096_d128", True, False, [(0, 0), (15, 15)]),
-    ("long_16k", True, False, [(1, 15)]),
-    ("padded_8k", False, True, [(0, 0), (7, 31), (3, 17)]),
+    ("gpt2_medium", True, False, 4),
+    ("n4096_d128", False, False, 4),
+    ("n4096_d128", True, False, 4),
+    ("long_16k", True, False, 0),
+    ("padded_8k", False, True, 4),
 ]
 
 
-@pytest.mark.parametrize("name,causal,precise,heads", FULL,
+def check_invariants(x, got, scale):
+    """Whole-tensor identities of the gradients, over every head, against
+    bounds from the rounding the kernels do.
+
+    sum_j dV_j = sum_i dO_i because every row of P sums to 1: the kernels
+    feed bf16(P) to the dV product, each P_ij rounded by at most 2^-9 of
+    itself, so per row sum_j bf16(P_ij) is within 2^-9 of 1 and per column c
+    the residual is at most 2^-9 sum_i |dO_ic| (asserted with a factor 2).
+
+    sum_j dK_j = 0 because every row of dS sums to 0 when D_i is exact. The
+    kernels take D_i from the bf16 output (each element within 2^-9 of the
+    fp32 one: |D error| <= 2^-9 ||dO_i|| ||O_i||) and round dS to bf16
+    (sum_j |bf16(dS_ij) - dS_ij| <= 2^-9 sum_j |dS_ij| <= 2^-9 (||dO_i||
+    max_j ||v_j|| + |D_i|), since |dP_ij| <= ||dO_i|| ||v_j||), so per column
+    |sum_j dK_jc| <= scale sum_i |q_ic| 2^-9 (||dO_i|| ||O_i|| + ||dO_i|| max_j
+    ||v_j|| + |D_i|) (asserted with a factor 2)."""
+    o, lse, dq, dk, dv = got
+    f64 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda().double()
+    q, v, do = f64(x["Q"]), f64(x["V"]), f64(x["dO"])
+    u = 2.0 ** -9
+    res_v = (dv.double().sum(dim=2) - do.sum(dim=2)).abs()
+    bound_v = 2 * u * do.abs().sum(dim=2)
+    od = o.double()
+    dnorm = do.norm(dim=3)
+    d_i = (do * od).sum(dim=3)
+    vmax = v.norm(dim=3).max(dim=2, keepdim=True).values
+    per_row = dnorm * od.norm(dim=3) + dnorm * vmax + d_i.abs()
+    res_k = dk.double().sum(dim=2).abs()
+    bound_k = 2 * u * scale * (q.abs() * per_row.unsqueeze(-1)).sum(dim=2)
+    rv, rk = float((res_v / bound_v).max()), float((res_k / bound_k).max())
+    log(f"  invariants: |sum dV - sum dO| max {float(res_v.max()):.3e} ({rv:.3f} of its bound), "
+        f"|sum dK| max {float(res_k.max()):.3e} ({rk:.3f} of its bound)")
+    assert rv <= 1.0, f"sum_j dV_j - sum_i dO_i exceeds its rounding bound ({rv:.3f})"
+    assert rk <= 1.0, f"sum_j dK_j exceeds its rounding bound ({rk:.3f})"
+
+
+@pytest.mark.parametrize("name,causal,precise,n_random", FULL,
                          ids=[f"{n}-{'causal' if c else 'full'}" for n, c, _, _ in FULL])
-def test_full_size_workload(name, causal, precise, heads):
+def test_full_size_workload(name, causal, precise, n_random):
     w = wl.WORKLOADS[name]
     log(f"full {name} causal={causal} precise={precise} B={w.B} H={w.H} N={w.N} d={w.d}")
     x = wl.workload_inputs(name)
     got = _run_bf16(x, causal, w.scale, x["kv_len"], precise=precise)
     for t in got:
         assert torch.isfinite(t).all()
-    # invariants over every head: sum_j dV_j = sum_i dO_i, sum_j dK_j = 0
-    dv_sum = got[4].double().sum(dim=2)
-    do_sum = torch.from_numpy(x["dO"]).cuda().double().sum(dim=2)
-    err_v = float((dv_sum - do_sum).abs().max())
-    err_k = float(got[3].double().sum(dim=2).abs().max())
-    log(f"  invariants: |sum dV - sum dO| max {err_v:.3e}, |sum dK| max {err_k:.3e}")
-    _check_heads(x, got, causal, w.scale, x["kv_len"], heads)
+    check_invariants(x, got, w.scale)
+    _check_heads(x, got, causal, w.scale, x["kv_len"], subset_heads(w.B, w.H, w.seed, n_random))
+
+
+def test_padded_default_mode_error_recorded():
+    """The padded workload's backward in the default mode, whose error on
+    its x8 outlier keys is above the absolute bar (about 0.15 on dQ and dK
+    and 0.1 on dV, from D taken from the bf16 output and from bf16 P and dS;
+    precise mode removes all three). Recorded so that a regression shows:
+    the forward is held to the usual bar, the gradients to err / max(1,
+    max |ref|) <= 2e-2 and max-abs <= 0.25."""
+    name = "padded_8k"
+    w = wl.WORKLOADS[name]
+    x = wl.workload_inputs(name)
+    got = _run_bf16(x, False, w.scale, x["kv_len"], precise=False)
+    o, lse, dq, dk, dv = got
+    for (b, h) in subset_heads(w.B, w.H, w.seed, 4):
+        L = int(x["kv_len"][b])
+        log(f"  default-mode head b={b} h={h} L={L}")
+        ro, rl = oracle.head_forward(x["Q"][b, h], x["K"][b, h], x["V"][b, h], w.scale, False, L)
+        compare("O", host(o[b, h]), ro)
+        compare_lse(host(lse[b, h]), rl)
+        rq, rk, rv = oracle.head_backward(x["Q"][b, h], x["K"][b, h], x["V"][b, h], x["dO"][b, h], w.scale,
+                                          False, L)
+        for nm, t, r in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+            err = np.abs(host(t[b, h]) - r)
+            mx, mn, top = float(err.max()), float(err.mean()), float(np.abs(r).max())
+            norm = mx / max(1.0, top)
+            log(f"    {nm:4s} max_abs={mx:.3e} mean_abs={mn:.3e} max|ref|={top:.3g} err/max(1,max|ref|)={norm:.3e}")
+            assert norm <= 2e-2, f"{nm}: normalised error {norm:.3e}"
+            assert mx <= 0.25, f"{nm}: max abs err {mx:.3e}"
