@@ -274,7 +274,8 @@ __global__ __launch_bounds__(256, D == 64 && !PRECISE && !DQ_ATOMIC && !DROP
   __shared__ __attribute__((aligned(16))) u16 dSs[DQ_ATOMIC ? NSPLIT * BQ * C::DSTR : 8];
   // V rows of the workgroup's keys (swizzled, read by rows as the B operand
   // of dP = dO V^T) when they are not held in registers.
-  __shared__ __attribute__((aligned(16))) u16 Vl[VLDS ? C::BKV * D : 8];
+  constexpr int VLSTR = D + 8;
+  __shared__ __attribute__((aligned(16))) u16 Vl[VLDS ? C::BKV * VLSTR : 8];
 
   // Causal grids pair key block i with block nkb - 1 - i in one workgroup,
   // the one with more query rows (the lower) first, so that every workgroup
@@ -320,11 +321,12 @@ __global__ __launch_bounds__(256, D == 64 && !PRECISE && !DQ_ATOMIC && !DROP
         kf[kk] = as_bf16x8(ld_buf16(rK, off));
         if constexpr (!VLDS) vf[kk] = as_bf16x8(ld_buf16(rV, off));
       }
-      if constexpr (VLDS) tile_to_lds<D, C::BKV, C::NW>(rV, kb0, Vl, w, lane);
+      if constexpr (VLDS) tile_to_lds_padded<D, VLSTR, C::BKV, C::NW>(rV, kb0, Vl, w, lane);
       // B operand of dP for d-chunk kk: this wave's key row 32w + r of Vl.
+      const u16* vrow = Vl + (32 * w + r) * VLSTR + 8 * g;
       auto vop = [&](int kk) {
         if constexpr (VLDS)
-          return ld_lds16(Vl + swz_off<D>(32 * w + r, 16 * kk + 8 * g));
+          return ld_lds16(vrow + 16 * kk);
         else
           return vf[kk];
       };
@@ -429,6 +431,16 @@ __global__ __launch_bounds__(256, D == 64 && !PRECISE && !DQ_ATOMIC && !DROP
               pa[qt] = mfma32(ld_lds16(Gt + o), vop(kk), pa[qt]);
             }
           }
+          if constexpr (VLDS) {
+            // Operand reads one d-chunk ahead of the products.
+            __builtin_amdgcn_sched_group_barrier(0x100, 7, 0);
+  #pragma unroll
+            for (int kk = 1; kk < D / 16; ++kk) {
+              __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+              __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          }
           // Masked scores become -inf, so their weights come out exactly 0.
           if ((kw0 + 31 >= kv_lim) || (causal && q0 < kw0 + 31)) {
             // Element e of tile qt is query q0 + 4g + c with the constant
@@ -497,6 +509,16 @@ __global__ __launch_bounds__(256, D == 64 && !PRECISE && !DQ_ATOMIC && !DROP
                 dk[t] = mfma32(aQ, dl[c], dk[t]);
               }
             }
+          if constexpr (VLDS) {
+            // Transposing reads two (t, c) steps ahead of the products.
+            __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+  #pragma unroll
+            for (int i = 2; i < (D / 32) * (BQ / 16); ++i) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+              __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+          }
           if constexpr (DQ_ATOMIC) {
             // dS (bf16, and its low half in precise mode) into the [query][key]
             // tile: slot s of chunk c is query 16c + 8(s/4) + 4g + s%4.
@@ -722,60 +744,79 @@ __global__ __launch_bounds__(256, PRECISE ? 1 : (D == 64 && !DROP ? 3 : 2)) void
       const int kb = it * BC;
       if (it + 1 < nt) load(kb + BC, P ? K0 : K1, P ? V0 : V1);
       if (it < nt_w) {
-        f32x16 s[BC / 32], dp[BC / 32];
+        // One 32-key half of the tile at a time: its score and dP products,
+        // mask, dS and dQ products, which keeps the live score registers to
+        // one half.
+        const bool need_mask = (kb + BC > kv_lim) || (causal && kb + BC - 1 > wave_q_first);
+        // Key kb + 4g + c, c = 32mt + 8(e/4) + e%4, is hidden iff c > lim.
+        const int lim = min(kv_lim - 1, causal ? q : kv_lim - 1) - (kb + 4 * g);
   #pragma unroll
         for (int mt = 0; mt < BC / 32; ++mt) {
           const int row = 32 * mt + r;
-          s[mt] = mfma32_first(ld_lds16(Kc + 32 * mt * KSTR + rw0), qf[0]);
-          dp[mt] = mfma32_first(ld_lds16(Vc + row * VSTR + 8 * g), df[0]);
+          f32x16 s = mfma32_first(ld_lds16(Kc + 32 * mt * KSTR + rw0), qf[0]);
+          f32x16 dp = mfma32_first(ld_lds16(Vc + row * VSTR + 8 * g), df[0]);
   #pragma unroll
           for (int kk = 1; kk < D / 16; ++kk) {
-            s[mt] = mfma32(ld_lds16(Kc + 32 * mt * KSTR + 32 * (kk >> 1) + ((kk & 1) ? rw1 : rw0)), qf[kk], s[mt]);
-            dp[mt] = mfma32(ld_lds16(Vc + row * VSTR + 16 * kk + 8 * g), df[kk], dp[mt]);
+            s = mfma32(ld_lds16(Kc + 32 * mt * KSTR + 32 * (kk >> 1) + ((kk & 1) ? rw1 : rw0)), qf[kk], s);
+            dp = mfma32(ld_lds16(Vc + row * VSTR + 16 * kk + 8 * g), df[kk], dp);
           }
-        }
-        if ((kb + BC > kv_lim) || (causal && kb + BC - 1 > wave_q_first)) {
-          // Key kb + 4g + c, c = 32mt + 8(e/4) + e%4, is hidden iff c > lim.
-          const int lim = min(kv_lim - 1, causal ? q : kv_lim - 1) - (kb + 4 * g);
+          if constexpr (!PRECISE && !DROP) {
+            // Operand reads two d-chunks ahead of the products.
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
   #pragma unroll
-          for (int mt = 0; mt < BC / 32; ++mt)
+            for (int i = 2; i < D / 16; ++i) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+              __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+          }
+          if (need_mask) {
   #pragma unroll
             for (int e = 0; e < 16; ++e) {
               const int c = 32 * mt + 8 * (e >> 2) + (e & 3);
-              s[mt][e] = c > lim ? -INFINITY : s[mt][e];
+              s[e] = c > lim ? -INFINITY : s[e];
             }
-        }
-  #pragma unroll
-        for (int mt = 0; mt < BC / 32; ++mt) {
+          }
           unsigned W[4];
           if constexpr (DROP) drop_words_query_lane(dpar, bh, q, kb + 32 * mt, g, lane, W);
   #pragma unroll
           for (int e = 0; e < 16; ++e) {
-            const float p = fast_exp2(s[mt][e] * sl2 - lse2);
+            const float p = fast_exp2(s[e] * sl2 - lse2);
             if constexpr (DROP)
-              dp[mt][e] = p * ((drop_keep(W, e, dpar.thresh) ? dp[mt][e] * dpar.keep_scale : 0.f) - Dq);
+              dp[e] = p * ((drop_keep(W, e, dpar.thresh) ? dp[e] * dpar.keep_scale : 0.f) - Dq);
             else
-              dp[mt][e] = p * (dp[mt][e] - Dq);
+              dp[e] = p * (dp[e] - Dq);
+          }
+          bf16x8 db[2], dl[PRECISE ? 2 : 1];
+  #pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            if constexpr (PRECISE)
+              pack_split_bf16x8(dp, 8 * h, db[h], dl[h]);
+            else
+              db[h] = pack_bf16x8(dp, 8 * h);
+          }
+          // dQ^T += K^T dS^T: A = K^T rows d = 32t + r, k-slots = keys of
+          // chunk c = 2mt + h.
+  #pragma unroll
+          for (int t = 0; t < D / 32; ++t)
+  #pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const int o = 16 * (2 * mt + h) * KSTR + 32 * t;
+              const bf16x8 aK = join_tr(ld_lds_tr(Kc + o + tw0), ld_lds_tr(Kc + o + tw1));
+              acc[t] = mfma32(aK, db[h], acc[t]);
+              if constexpr (PRECISE) acc[t] = mfma32(aK, dl[h], acc[t]);
+            }
+          if constexpr (!PRECISE && !DROP) {
+            // Transposing reads two products ahead.
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+  #pragma unroll
+            for (int i = 2; i < D / 32 * 2; ++i) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
           }
         }
-        bf16x8 db[BC / 16], dl[PRECISE ? BC / 16 : 1];
-  #pragma unroll
-        for (int c = 0; c < BC / 16; ++c) {
-          if constexpr (PRECISE)
-            pack_split_bf16x8(dp[c >> 1], 8 * (c & 1), db[c], dl[c]);
-          else
-            db[c] = pack_bf16x8(dp[c >> 1], 8 * (c & 1));
-        }
-        // dQ^T += K^T dS^T: A = K^T rows d = 32t + r, k-slots = keys of chunk c.
-  #pragma unroll
-        for (int t = 0; t < D / 32; ++t)
-  #pragma unroll
-          for (int c = 0; c < BC / 16; ++c) {
-            const int o = 16 * c * KSTR + 32 * t;
-            const bf16x8 aK = join_tr(ld_lds_tr(Kc + o + tw0), ld_lds_tr(Kc + o + tw1));
-            acc[t] = mfma32(aK, db[c], acc[t]);
-            if constexpr (PRECISE) acc[t] = mfma32(aK, dl[c], acc[t]);
-          }
       }
       // Each wave waits for its own loads before the barrier publishes them.
       wait_vmem_all();
