@@ -10,8 +10,9 @@
 // bandwidth-bound pre-pass computes from O and dO (default), or, with
 // FA_BWD_PRECISE, a separate recompute pass sums P o dP exactly.
 //
-// Main kernel (one workgroup per 128 keys of one (b, h), two such key blocks
-// in causal grids, 4 waves of 32 keys):
+// Key-outer kernel (one workgroup per 128 keys of one (b, h), two such key
+// blocks in causal grids, 4 waves of 32 keys; the plain d=128 instance runs
+// 8 waves on 256 keys and keeps V in LDS, see below):
 //   * the wave's K and V rows sit in registers as the B operands of
 //     S = Q K^T and dP = dO V^T (32x32x16 bf16 products, fp32 accumulate);
 //   * query blocks (64 rows at d=128, 32 at d=64) stream through LDS, stored both row-major
@@ -224,6 +225,7 @@ struct DkdvCfg {
   // Query rows per block. At d=64 blocks of 32 rows keep the plain kernel
   // within 168 VGPRs, i.e. three waves per SIMD (backward +3% at N=1024 and
   // N=8192); at d=128 (one wave per SIMD) 32-row blocks measured 4% slower.
+  // (The plain d=128 instance overrides NW and BQ: dkdv_waves below.)
   static constexpr int BQ = D == 64 ? 32 : 64;
   // Q and dO tile row stride (elements) of the xpad layout (xpad_off): both
   // tiles are read row-wise and transposed, conflict-free in that layout.
@@ -241,13 +243,18 @@ struct DkdvCfg {
 // DROP: fused dropout regenerated from the generator state (fa_dropout.h):
 // dV takes the kept weights, dP of kept elements is scaled by the keep
 // factor and dropped ones contribute only the -P D term of dS.
-// The plain d=128 instance keeps V in LDS instead of registers and takes
-// query blocks of 32 rows: its registers then fit two waves per SIMD.
+// The plain d=128 instance keeps V in LDS instead of registers and computes
+// 32 query rows at a time: its registers then fit two waves per SIMD. It
+// runs eight waves (256 keys) per workgroup, one workgroup per CU, on blocks
+// of 64 query rows, so that each block brought into LDS (and each barrier)
+// serves twice the products of a four-wave workgroup.
 template <int D, bool PRECISE, bool DQ_ATOMIC, bool DROP>
 constexpr bool dkdv_v_in_lds() { return D == 128 && !PRECISE && !DQ_ATOMIC && !DROP; }
+template <int D, bool PRECISE, bool DQ_ATOMIC, bool DROP>
+constexpr int dkdv_waves() { return dkdv_v_in_lds<D, PRECISE, DQ_ATOMIC, DROP>() ? 8 : DkdvCfg<D>::NW; }
 
 template <int D, bool PRECISE, bool DQ_ATOMIC, bool DROP = false>
-__global__ __launch_bounds__(256, D == 64 && !PRECISE && !DQ_ATOMIC && !DROP
+__global__ __launch_bounds__((64 * dkdv_waves<D, PRECISE, DQ_ATOMIC, DROP>()), D == 64 && !PRECISE && !DQ_ATOMIC && !DROP
                                       ? 3
                                       : (dkdv_v_in_lds<D, PRECISE, DQ_ATOMIC, DROP>() ? 2 : 1)) void bwd_dkdv_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
@@ -256,7 +263,9 @@ __global__ __launch_bounds__(256, D == 64 && !PRECISE && !DQ_ATOMIC && !DROP
     float sl2, int causal, const int32_t* __restrict__ kv_len, int nkb, int total, DropParams dpar) {
   using C = DkdvCfg<D>;
   constexpr bool VLDS = dkdv_v_in_lds<D, PRECISE, DQ_ATOMIC, DROP>();
-  constexpr int BQ = VLDS ? 32 : C::BQ;
+  constexpr int NW = dkdv_waves<D, PRECISE, DQ_ATOMIC, DROP>();
+  constexpr int BKV = 32 * NW;
+  constexpr int BQ = VLDS ? 64 : C::BQ;
   constexpr int NSPLIT = PRECISE ? 2 : 1;
   constexpr int QSTR = C::QSTR;
   // Q and dO blocks arrive by direct-to-LDS loads into padded tiles. The two
@@ -275,7 +284,7 @@ __global__ __launch_bounds__(256, D == 64 && !PRECISE && !DQ_ATOMIC && !DROP
   // V rows of the workgroup's keys (swizzled, read by rows as the B operand
   // of dP = dO V^T) when they are not held in registers.
   constexpr int VLSTR = D + 8;
-  __shared__ __attribute__((aligned(16))) u16 Vl[VLDS ? C::BKV * VLSTR : 8];
+  __shared__ __attribute__((aligned(16))) u16 Vl[VLDS ? BKV * VLSTR : 8];
 
   // Causal grids pair key block i with block nkb - 1 - i in one workgroup,
   // the one with more query rows (the lower) first, so that every workgroup
@@ -288,7 +297,7 @@ __global__ __launch_bounds__(256, D == 64 && !PRECISE && !DQ_ATOMIC && !DROP
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, r = lane & 31, g = lane >> 5;
   auto block = [&](const int kbi) {
-    const int kb0 = kbi * C::BKV;
+    const int kb0 = kbi * BKV;
     const int kw0 = kb0 + 32 * w;
     const int key = kw0 + r;
     const size_t head = (size_t)bh * N * D;
@@ -321,7 +330,7 @@ __global__ __launch_bounds__(256, D == 64 && !PRECISE && !DQ_ATOMIC && !DROP
         kf[kk] = as_bf16x8(ld_buf16(rK, off));
         if constexpr (!VLDS) vf[kk] = as_bf16x8(ld_buf16(rV, off));
       }
-      if constexpr (VLDS) tile_to_lds_padded<D, VLSTR, C::BKV, C::NW>(rV, kb0, Vl, w, lane);
+      if constexpr (VLDS) tile_to_lds_padded<D, VLSTR, BKV, NW>(rV, kb0, Vl, w, lane);
       // B operand of dP for d-chunk kk: this wave's key row 32w + r of Vl.
       const u16* vrow = Vl + (32 * w + r) * VLSTR + 8 * g;
       auto vop = [&](int kk) {
@@ -353,13 +362,13 @@ __global__ __launch_bounds__(256, D == 64 && !PRECISE && !DQ_ATOMIC && !DROP
       // statistics raw into registers (scaled when stored).
       auto load = [&](int q0, u16* Qt, u16* Gt) {
         if constexpr (VLDS) {
-          // 32-row tiles are ten 1 KB blocks each: waves 0-1 fill the Q tile
-          // and waves 2-3 the dO tile, five blocks per wave.
+          // 64-row tiles are twenty 1 KB blocks each: waves 0-3 fill the Q
+          // tile and waves 4-7 the dO tile, five blocks per wave.
           const int ws = __builtin_amdgcn_readfirstlane(w);
-          if (ws < 2)
-            tile_to_lds_xpad<D, QSTR, BQ, 2>(rQ, q0, Qt, ws, lane);
+          if (ws < NW / 2)
+            tile_to_lds_xpad<D, QSTR, BQ, NW / 2>(rQ, q0, Qt, ws, lane);
           else
-            tile_to_lds_xpad<D, QSTR, BQ, 2>(rO, q0, Gt, ws - 2, lane);
+            tile_to_lds_xpad<D, QSTR, BQ, NW / 2>(rO, q0, Gt, ws - NW / 2, lane);
         } else {
           tile_to_lds_xpad<D, QSTR, BQ, C::NW>(rQ, q0, Qt, w, lane);
           tile_to_lds_xpad<D, QSTR, BQ, C::NW>(rO, q0, Gt, w, lane);
@@ -404,7 +413,89 @@ __global__ __launch_bounds__(256, D == 64 && !PRECISE && !DQ_ATOMIC && !DROP
         const int q0 = qb * BQ;
         if (qb + 1 < nqb) load(q0 + BQ, buf ? Q0 : Q1, buf ? G0 : G1);
 
-        if ((kw0 < kv_lim) && (!causal || q0 + BQ - 1 >= kw0)) {
+        if constexpr (VLDS) {
+          // 32 query rows at a time (sub-block sb: rows q0 + 32sb ..).
+  #pragma unroll
+          for (int sb = 0; sb < BQ / 32; ++sb) {
+            const int qs = q0 + 32 * sb;
+            if (!((kw0 < kv_lim) && (!causal || qs + 31 >= kw0))) continue;
+            const int rb = 32 * sb * QSTR;
+            // S = Q K^T, dP = dO V^T: rows = queries qs + 8i + 4g + j, column
+            // = key; dP accumulates onto -D_i of its row.
+            f32x16 sa = mfma32_first(ld_lds16(Qt + rb + rw0), kf[0]);
+            f32x16 pa;
+            {
+              f32x16 nd;
+  #pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const f32x4 d4 = *reinterpret_cast<const f32x4*>(&Ds[buf][32 * sb + 8 * i + 4 * g]);
+  #pragma unroll
+                for (int j = 0; j < 4; ++j) nd[4 * i + j] = d4[j];
+              }
+              pa = mfma32(ld_lds16(Gt + rb + rw0), vop(0), nd);
+            }
+  #pragma unroll
+            for (int kk = 1; kk < D / 16; ++kk) {
+              const int o = rb + 32 * (kk >> 1) + ((kk & 1) ? rw1 : rw0);
+              sa = mfma32(ld_lds16(Qt + o), kf[kk], sa);
+              pa = mfma32(ld_lds16(Gt + o), vop(kk), pa);
+            }
+            // Operand reads one d-chunk ahead of the products.
+            __builtin_amdgcn_sched_group_barrier(0x100, 7, 0);
+  #pragma unroll
+            for (int kk = 1; kk < D / 16; ++kk) {
+              __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+              __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            if ((kw0 + 31 >= kv_lim) || (causal && qs < kw0 + 31)) {
+              // Element e is query qs + 4g + c, c = 8(e/4) + e%4; hidden iff c < lim.
+              const int lim = key >= kv_lim ? INT_MAX : (causal ? key - qs - 4 * g : INT_MIN);
+  #pragma unroll
+              for (int e = 0; e < 16; ++e) {
+                const int c = 8 * (e >> 2) + (e & 3);
+                sa[e] = c < lim ? -INFINITY : sa[e];
+              }
+            }
+  #pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse2s[buf][32 * sb + 8 * i + 4 * g]);
+  #pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const int e = 4 * i + j;
+                const float p = fast_exp2(sa[e] * sl2 - l4[j]);
+                sa[e] = p;
+                pa[e] = p * pa[e];
+              }
+            }
+            bf16x8 pb[2], db[2];
+  #pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              pb[h] = pack_bf16x8(sa, 8 * h);
+              db[h] = pack_bf16x8(pa, 8 * h);
+            }
+            // dV^T += dO^T P, dK^T += Q^T dS over the sub-block's query
+            // chunks c = 2sb + h.
+  #pragma unroll
+            for (int t = 0; t < D / 32; ++t)
+  #pragma unroll
+              for (int h = 0; h < 2; ++h) {
+                const int o = 16 * (2 * sb + h) * QSTR + 32 * t;
+                const bf16x8 aO = join_tr(ld_lds_tr(Gt + o + tw0), ld_lds_tr(Gt + o + tw1));
+                const bf16x8 aQ = join_tr(ld_lds_tr(Qt + o + tw0), ld_lds_tr(Qt + o + tw1));
+                dv[t] = mfma32(aO, pb[h], dv[t]);
+                dk[t] = mfma32(aQ, db[h], dk[t]);
+              }
+            // Transposing reads two (t, h) steps ahead of the products.
+            __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+  #pragma unroll
+            for (int i = 2; i < (D / 32) * 2; ++i) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+              __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+          }
+        } else if ((kw0 < kv_lim) && (!causal || q0 + BQ - 1 >= kw0)) {
           // S = Q K^T, dP = dO V^T: rows = queries 32*qt + 8i + 4g + j, column = key.
           f32x16 sa[BQ / 32], pa[BQ / 32];
   #pragma unroll
@@ -430,16 +521,6 @@ __global__ __launch_bounds__(256, D == 64 && !PRECISE && !DQ_ATOMIC && !DROP
               sa[qt] = mfma32(ld_lds16(Qt + o), kf[kk], sa[qt]);
               pa[qt] = mfma32(ld_lds16(Gt + o), vop(kk), pa[qt]);
             }
-          }
-          if constexpr (VLDS) {
-            // Operand reads one d-chunk ahead of the products.
-            __builtin_amdgcn_sched_group_barrier(0x100, 7, 0);
-  #pragma unroll
-            for (int kk = 1; kk < D / 16; ++kk) {
-              __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
-              __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
           }
           // Masked scores become -inf, so their weights come out exactly 0.
           if ((kw0 + 31 >= kv_lim) || (causal && q0 < kw0 + 31)) {
@@ -509,16 +590,6 @@ __global__ __launch_bounds__(256, D == 64 && !PRECISE && !DQ_ATOMIC && !DROP
                 dk[t] = mfma32(aQ, dl[c], dk[t]);
               }
             }
-          if constexpr (VLDS) {
-            // Transposing reads two (t, c) steps ahead of the products.
-            __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
-  #pragma unroll
-            for (int i = 2; i < (D / 32) * (BQ / 16); ++i) {
-              __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-              __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-          }
           if constexpr (DQ_ATOMIC) {
             // dS (bf16, and its low half in precise mode) into the [query][key]
             // tile: slot s of chunk c is query 16c + 8(s/4) + 4g + s%4.
@@ -717,6 +788,9 @@ __global__ __launch_bounds__(256, PRECISE ? 1 : (D == 64 && !DROP ? 3 : 2)) void
     for (int t = 0; t < D / 32; ++t)
   #pragma unroll
       for (int e = 0; e < 16; ++e) acc[t][e] = 0.f;
+    f32x16 ndq;
+  #pragma unroll
+    for (int e = 0; e < 16; ++e) ndq[e] = -Dq;
 
     auto load = [&](int kb, u16* Kt, u16* Vt) {
       tile_to_lds_xpad<D, KSTR, BC, C::NW>(rK, kb, Kt, w, lane);
@@ -754,7 +828,10 @@ __global__ __launch_bounds__(256, PRECISE ? 1 : (D == 64 && !DROP ? 3 : 2)) void
         for (int mt = 0; mt < BC / 32; ++mt) {
           const int row = 32 * mt + r;
           f32x16 s = mfma32_first(ld_lds16(Kc + 32 * mt * KSTR + rw0), qf[0]);
-          f32x16 dp = mfma32_first(ld_lds16(Vc + row * VSTR + 8 * g), df[0]);
+          // Plain mode: the dP product accumulates onto -D_i, so that
+          // dS = P (dP - D_i) is one multiply.
+          f32x16 dp = (PRECISE || DROP) ? mfma32_first(ld_lds16(Vc + row * VSTR + 8 * g), df[0])
+                                        : mfma32(ld_lds16(Vc + row * VSTR + 8 * g), df[0], ndq);
   #pragma unroll
           for (int kk = 1; kk < D / 16; ++kk) {
             s = mfma32(ld_lds16(Kc + 32 * mt * KSTR + 32 * (kk >> 1) + ((kk & 1) ? rw1 : rw0)), qf[kk], s);
@@ -784,8 +861,10 @@ __global__ __launch_bounds__(256, PRECISE ? 1 : (D == 64 && !DROP ? 3 : 2)) void
             const float p = fast_exp2(s[e] * sl2 - lse2);
             if constexpr (DROP)
               dp[e] = p * ((drop_keep(W, e, dpar.thresh) ? dp[e] * dpar.keep_scale : 0.f) - Dq);
-            else
+            else if constexpr (PRECISE)
               dp[e] = p * (dp[e] - Dq);
+            else
+              dp[e] = p * dp[e];
           }
           bf16x8 db[2], dl[PRECISE ? 2 : 1];
   #pragma unroll
@@ -853,9 +932,10 @@ template <int D, bool PRECISE, bool DQ_ATOMIC, bool DROP = false>
 static void launch_dkdv(const u16* q, const u16* k, const u16* v, const u16* g, const float* LSE,
                         const float* Dws, float* dQ, float* dK, float* dV, const AttnShape& s, float sl2,
                         hipStream_t stream, DropParams dp = {}) {
-  const int nkb = (s.N + DkdvCfg<D>::BKV - 1) / DkdvCfg<D>::BKV;
+  constexpr int NW = dkdv_waves<D, PRECISE, DQ_ATOMIC, DROP>();
+  const int nkb = (s.N + 32 * NW - 1) / (32 * NW);
   const int total = s.B * s.H * (s.causal ? (nkb + 1) / 2 : nkb);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, PRECISE, DQ_ATOMIC, DROP>), dim3(total), dim3(256), 0, stream, q, k, v,
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, PRECISE, DQ_ATOMIC, DROP>), dim3(total), dim3(64 * NW), 0, stream, q, k, v,
                      g, LSE, Dws, dQ, dK, dV, s.H, s.N, s.scale, sl2, s.causal, s.kv_len, nkb, total, dp);
 }
 

@@ -177,8 +177,13 @@ def test_p_zero_matches_plain_entry_points(d, causal):
     assert torch.equal(O0, O1) and torch.equal(L0, L1)
     g0 = fa.flash_attn_bwd(dev["Q"], dev["K"], dev["V"], O0, dev["dO"], L0, causal=causal)
     g1 = fa.flash_attn_bwd_dropout(dev["Q"], dev["K"], dev["V"], O0, dev["dO"], L0, 0.0, 99, 0, causal=causal)
+    # The plain dQ kernel accumulates dP onto -D_i inside the matrix product,
+    # the dropout kernel subtracts D_i afterwards: dS_ij can round to
+    # neighbouring bf16 values, which moves the gradients by a few bf16 ulps
+    # of dS (far below the parity tolerance; a mask applied at p = 0 would
+    # move them by O(1)).
     for a, b in zip(g0, g1):
-        assert float((a - b).abs().max()) <= 1e-6 * max(1.0, float(a.abs().max()))
+        assert float((a - b).abs().max()) <= 2e-3 * max(1.0, float(a.abs().max()))
 
 
 def test_reproducible_and_offset_draws_new_mask():
