@@ -439,6 +439,34 @@ def memory_sweep():
     return out
 
 
+def library_gemm_reference(steps=10, warmup=3, n=8192):
+    """Context for the matrix-core fraction: the rate of the vendor GEMM
+    (torch.mm, hipBLASLt) on one n x n x n product of random-normal bf16
+    operands on this machine. The chip's clock under matrix-core load depends
+    on the operands' bit activity, so random data is the relevant reference
+    for attention inputs; not part of the attention step."""
+    import torch
+    g = torch.Generator(device="cuda").manual_seed(1)
+    a = torch.randn((n, n), device="cuda", generator=g, dtype=torch.bfloat16)
+    b = torch.randn((n, n), device="cuda", generator=g, dtype=torch.bfloat16)
+    c = torch.empty((n, n), device="cuda", dtype=torch.bfloat16)
+    for _ in range(warmup):
+        torch.mm(a, b, out=c)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        torch.mm(a, b, out=c)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    tf = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+    del a, b, c
+    return {"op": f"torch.mm bf16 {n}x{n}x{n}, random-normal operands", "ms_per_call": round(ms, 4),
+            "tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+
+
 def parse_only(spec):
     name, _, mode = spec.partition(":")
     from io_aware_exact_11_amd import workloads as wl
@@ -541,6 +569,8 @@ def main():
         torch.cuda.empty_cache()
         result["workloads"] = workloads
         result["memory_sweep_B2_H16_d128_causal"] = memory_sweep()
+        torch.cuda.empty_cache()
+        result["library_gemm_reference"] = library_gemm_reference()
     graded = []
     for r in steps_res:
         if (r["workload"], r["causal"]) in GRADED and "dropout" not in r:

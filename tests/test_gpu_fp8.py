@@ -97,12 +97,15 @@ def test_fp8_loses_less_than_naive_8bit_attention():
     O, _ = fa.flash_attn_fwd_fp8(_dev(x["Q8"]), _dev(x["K8"]), _dev(x["Vt8"]), x["dq"], x["dk"], x["dv"], scale=scale)
     torch.cuda.synchronize()
     Oh = host(O)
-    ours, naive = [], []
+    ours, naive, floor = [], [], []
     for h in range(H):
         exact, _ = oracle.head_forward(x["Q"][0, h], x["K"][0, h], x["V"][0, h], scale)
         q = of.e4m3_decode(x["Q8"][0, h]) * x["dq"]
         k = of.e4m3_decode(x["K8"][0, h]) * x["dk"]
         v = of.e4m3_decode(x["Vt8"][0, h]).T * x["dv"]
+        # Input quantisation alone: exact attention (fp64) on the decoded 8-bit inputs.
+        deq, _ = oracle.head_forward(q, k, v, scale)
+        floor.append(np.sqrt(np.mean((deq - exact) ** 2)))
         S = np.float32(scale) * (q @ k.T)
         fs = np.abs(S).max() / 448.0
         S8 = of.e4m3_decode(of.e4m3_encode(S / fs)) * fs
@@ -112,8 +115,13 @@ def test_fp8_loses_less_than_naive_8bit_attention():
         ours.append(np.sqrt(np.mean((Oh[0, h] - exact) ** 2)))
         naive.append(np.sqrt(np.mean((P8 @ v - exact) ** 2)))
     ratio = np.mean(naive) / np.mean(ours)
-    log(f"    rms error: kernel {np.mean(ours):.3e}, naive 8-bit {np.mean(naive):.3e}, ratio {ratio:.2f}")
-    assert ratio > 1.0
+    over_floor = np.mean(ours) / np.mean(floor)
+    log(f"    rms error: kernel {np.mean(ours):.3e}, naive 8-bit {np.mean(naive):.3e}, ratio {ratio:.2f}; "
+        f"input quantisation alone {np.mean(floor):.3e} (kernel / that {over_floor:.3f})")
+    # The kernel keeps scores and weights in fp32/bf16, so nearly all of its error is the 8-bit rounding of
+    # its inputs, which the naive path shares; the naive path's E4M3 scores and weights add the rest.
+    assert over_floor <= 1.1, f"kernel error {over_floor:.3f}x the input-quantisation error"
+    assert ratio >= 1.2, f"naive / kernel error ratio {ratio:.2f}"
 
 
 def test_full_size_n4096_d128_fp8_workload():
