@@ -70,6 +70,10 @@ SMALL = [
     (1, 2, 130, 128, False, False, False),
     (2, 2, 300, 64, True, False, True),
     (2, 2, 300, 128, False, False, True),
+    # d=128 across the 256-key blocks of the key-outer kernel and the
+    # 128-row query blocks: one key past two blocks, and a ragged third block
+    (1, 2, 513, 128, True, False, False),
+    (1, 2, 700, 128, False, False, False),
 ]
 
 
@@ -95,15 +99,25 @@ def test_edge_lengths(N, d, causal):
     _check_heads(x, got, causal, scale, None, [(0, 0), (0, 1)])
 
 
-def test_kv_len_edge_values():
-    """kv_len = 0 (all keys masked), 1, a tile boundary, N, and values
-    outside [0, N] that the kernels clamp."""
-    B, H, N, d = 6, 1, 200, 64
-    kv = np.array([0, 1, 64, 200, 999, -5], np.int32)
+KV_EDGES = {
+    # d: (N, kv_len per batch row): 0 (all keys masked), 1, tile and block
+    # boundaries (64-key tiles; 128- and 256-key blocks of the key-outer
+    # kernel), N, and values outside [0, N] that the kernels clamp
+    64: (200, [0, 1, 64, 200, 999, -5]),
+    128: (600, [0, 1, 255, 256, 257, 600, 999, -5]),
+}
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_kv_len_edge_values(d):
+    """Key padding at its edge values, causal and not."""
+    N, kv_list = KV_EDGES[d]
+    B, H = len(kv_list), 1
+    kv = np.array(kv_list, np.int32)
     clamped = np.clip(kv, 0, N)
-    log(f"kv_len edges {kv.tolist()}")
-    x = wl.make_inputs(B, H, N, d, seed=11)
-    scale = 0.125
+    log(f"kv_len edges d={d} N={N} {kv.tolist()}")
+    x = wl.make_inputs(B, H, N, d, seed=11 + d)
+    scale = 0.125 if d == 64 else float(np.float32(d ** -0.5))
     for causal in (False, True):
         o, lse, dq, dk, dv = _run_bf16(x, causal, scale, kv)
         for b in range(B):
