@@ -224,8 +224,9 @@ struct DkdvCfg {
   static constexpr int BKV = 32 * NW;          // keys per workgroup (32 per wave)
   // Query rows per block. At d=64 blocks of 32 rows keep the plain kernel
   // within 168 VGPRs, i.e. three waves per SIMD (backward +3% at N=1024 and
-  // N=8192); at d=128 (one wave per SIMD) 32-row blocks measured 4% slower.
-  // (The plain d=128 instance overrides NW and BQ: dkdv_waves below.)
+  // N=8192); the d=128 instances that hold K and V in registers run one wave
+  // per SIMD, where 32-row blocks measured 4% slower. (The plain d=128
+  // instance overrides NW and BQ: dkdv_waves below.)
   static constexpr int BQ = D == 64 ? 32 : 64;
   // Q and dO tile row stride (elements) of the xpad layout (xpad_off): both
   // tiles are read row-wise and transposed, conflict-free in that layout.
@@ -234,8 +235,9 @@ struct DkdvCfg {
   static constexpr int DSTR = BKV + 8;         // dS tile row stride (row reads only)
 };
 
-// dK, dV for 128 keys of one (b, h). The wave's K and V rows are B operands
-// held in registers; query blocks of Q and dO stream through swizzled,
+// dK, dV for 32 keys per wave of one (b, h) (128 or 256 keys per workgroup).
+// The wave's K and V rows are B operands held in registers (V in LDS in the
+// plain d=128 instance); query blocks of Q and dO stream through swizzled,
 // double-buffered LDS tiles that serve as A operands both row-wise
 // (S = Q K^T, dP = dO V^T) and transposed (dV^T = dO^T P, dK^T = Q^T dS,
 // through ds_read_b64_tr_b16), with P and dS taken from registers.
