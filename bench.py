@@ -101,13 +101,14 @@ def stored_traffic(key):
 class Case:
     """Device-resident inputs and outputs of one workload."""
 
-    def __init__(self, name, causal, precise=False, dropout=None):
+    def __init__(self, name, causal, precise=False, dropout=None, dq_atomic=False):
         import torch
         from io_aware_exact_11_amd import workloads as wl
         import io_aware_exact_11_amd as fa
         self.fa = fa
         self.w = wl.WORKLOADS[name]
         self.name, self.causal, self.precise, self.dropout = name, causal, precise, dropout
+        self.dq_atomic = dq_atomic
         x = wl.workload_inputs(name)
         dev = lambda bits: torch.from_numpy(bits.view("int16")).view(torch.bfloat16).cuda()
         self.q, self.k, self.v, self.do = (dev(x[n + "_bits"]) for n in ("Q", "K", "V", "dO"))
@@ -142,7 +143,7 @@ class Case:
             return
         self.fa.flash_attn_bwd(self.q, self.k, self.v, self.o, self.do, self.lse, causal=self.causal,
                                scale=self.w.scale, kv_len=self.kv, precise=self.precise,
-                               dq=self.dq, dk=self.dk, dv=self.dv, workspace=self.ws)
+                               dq_atomic=self.dq_atomic, dq=self.dq, dk=self.dk, dv=self.dv, workspace=self.ws)
 
     def run(self, steps, warmup):
         """Time exactly `steps` whole steps after `warmup` untimed ones. The
@@ -190,7 +191,8 @@ def measure(case, steps, warmup):
     step_t = (ff + fb) / (wms * 1e-3) / 1e12
     w = case.w
     return {"workload": case.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": case.causal,
-            "padded": case.kv_host is not None, "bwd_mode": "precise" if case.precise else "default",
+            "padded": case.kv_host is not None,
+            "bwd_mode": ("precise" if case.precise else "default") + (", atomic dQ" if case.dq_atomic else ""),
             **({"dropout": case.dropout} if case.dropout else {}),
             "pairs": case.pairs, "ms_per_step": round(wms, 4), "fwd_ms": round(fms, 4), "bwd_ms": round(bms, 4),
             "fwd_tflops": round(fwd_t, 2), "fwd_frac": round(fwd_t / PEAK_BF16_TFLOPS, 4),
@@ -206,7 +208,15 @@ def rooflines(case, res):
     bwd_ach = fb / (res["bwd_ms"] * 1e-3) / 1e12
     fwd_ach = ff / (res["fwd_ms"] * 1e-3) / 1e12
     d = case.w.d
-    bwd = {"kernel": f"flash_attn_bwd call: bwd_dq_kernel<{d}> then bwd_dkdv_kernel<{d}>",
+    if case.dq_atomic:
+        tr = {"fwd_bytes": tr.get("fwd_bytes")}  # the stored backward bytes are the split mode's
+    if case.dq_atomic:
+        bwd_kernels = f"dQ zero fill, bwd_dot_kernel<{d}>, bwd_dkdv_kernel<{d}> with atomic dQ"
+    elif case.precise:
+        bwd_kernels = f"bwd_exact_d_kernel<{d}>, bwd_dq_kernel<{d}>, bwd_dkdv_kernel<{d}> (precise)"
+    else:
+        bwd_kernels = f"bwd_dq_kernel<{d}> then bwd_dkdv_kernel<{d}>"
+    bwd = {"kernel": f"flash_attn_bwd call: {bwd_kernels}",
            "bound": "mfma", "achieved": round(bwd_ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
            "frac": round(bwd_ach / PEAK_BF16_TFLOPS, 4), "traffic": tr.get("bwd_call_bytes"),
            "algorithmic_flops_per_launch": fb, "avg_launch_ms": res["bwd_ms"]}
@@ -485,6 +495,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--only", default=None, help="time one step workload NAME[:c|:nc] only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--dq-atomic", action="store_true",
+                    help="with --only: run the backward with FA_BWD_DQ_ATOMIC (dQ by fp32 atomics), for comparison")
     ap.add_argument("--no-extra", action="store_true", help="headline workload only")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run one device-to-device copy of this many MiB (HBM counter calibration)")
@@ -518,7 +530,9 @@ def main():
         extra_steps = [] if args.no_extra else [s for s in STEP_WORKLOADS if s is not head]
 
     print(f"bench: {case_key(*head[:2])} ({args.steps} steps)", file=sys.stderr, flush=True)
-    case = Case(head[0], head[1], precise=head[2])
+    if args.dq_atomic and not args.only:
+        raise SystemExit("bench.py: --dq-atomic needs --only (it is a comparison run, not the headline)")
+    case = Case(head[0], head[1], precise=head[2], dq_atomic=args.dq_atomic)
     res = measure(case, args.steps, args.warmup)
     roof_bwd, roof_fwd = rooflines(case, res)
     describe = case.describe()
