@@ -11,8 +11,9 @@
 // FA_BWD_PRECISE, a separate recompute pass sums P o dP exactly.
 //
 // Key-outer kernel (one workgroup per 128 keys of one (b, h), two such key
-// blocks in causal grids, 4 waves of 32 keys; the plain d=128 instance runs
-// 8 waves on 256 keys and keeps V in LDS, see below):
+// blocks in causal grids, 4 waves of 32 keys; the d=128 instances without
+// the precise or atomic-dQ modes run 8 waves on 256 keys and keep V in LDS,
+// see below):
 //   * the wave's K and V rows sit in registers as the B operands of
 //     S = Q K^T and dP = dO V^T (32x32x16 bf16 products, fp32 accumulate);
 //   * query blocks (64 rows at d=128, 32 at d=64) stream through LDS, stored both row-major
@@ -225,8 +226,8 @@ struct DkdvCfg {
   // Query rows per block. At d=64 blocks of 32 rows keep the plain kernel
   // within 168 VGPRs, i.e. three waves per SIMD (backward +3% at N=1024 and
   // N=8192); the d=128 instances that hold K and V in registers run one wave
-  // per SIMD, where 32-row blocks measured 4% slower. (The plain d=128
-  // instance overrides NW and BQ: dkdv_waves below.)
+  // per SIMD, where 32-row blocks measured 4% slower. (The d=128 instances
+  // with V in LDS override NW and BQ: dkdv_waves below.)
   static constexpr int BQ = D == 64 ? 32 : 64;
   // Q and dO tile row stride (elements) of the xpad layout (xpad_off): both
   // tiles are read row-wise and transposed, conflict-free in that layout.
@@ -237,21 +238,23 @@ struct DkdvCfg {
 
 // dK, dV for 32 keys per wave of one (b, h) (128 or 256 keys per workgroup).
 // The wave's K and V rows are B operands held in registers (V in LDS in the
-// plain d=128 instance); query blocks of Q and dO stream through swizzled,
-// double-buffered LDS tiles that serve as A operands both row-wise
-// (S = Q K^T, dP = dO V^T) and transposed (dV^T = dO^T P, dK^T = Q^T dS,
-// through ds_read_b64_tr_b16), with P and dS taken from registers.
+// d=128 instances without precise or atomic-dQ mode); query blocks of Q and
+// dO stream through swizzled, double-buffered LDS tiles that serve as A
+// operands both row-wise (S = Q K^T, dP = dO V^T) and transposed
+// (dV^T = dO^T P, dK^T = Q^T dS, through ds_read_b64_tr_b16), with P and dS
+// taken from registers.
 //
 // DROP: fused dropout regenerated from the generator state (fa_dropout.h):
 // dV takes the kept weights, dP of kept elements is scaled by the keep
 // factor and dropped ones contribute only the -P D term of dS.
-// The plain d=128 instance keeps V in LDS instead of registers and computes
-// 32 query rows at a time: its registers then fit two waves per SIMD. It
+// The d=128 instance (plain or with dropout) keeps V in LDS instead of
+// registers and computes 32 query rows at a time: its registers then fit
+// two waves per SIMD (the dropout one with a few spilled registers). It
 // runs eight waves (256 keys) per workgroup, one workgroup per CU, on blocks
 // of 64 query rows, so that each block brought into LDS (and each barrier)
 // serves twice the products of a four-wave workgroup.
 template <int D, bool PRECISE, bool DQ_ATOMIC, bool DROP>
-constexpr bool dkdv_v_in_lds() { return D == 128 && !PRECISE && !DQ_ATOMIC && !DROP; }
+constexpr bool dkdv_v_in_lds() { return D == 128 && !PRECISE && !DQ_ATOMIC; }
 template <int D, bool PRECISE, bool DQ_ATOMIC, bool DROP>
 constexpr int dkdv_waves() { return dkdv_v_in_lds<D, PRECISE, DQ_ATOMIC, DROP>() ? 8 : DkdvCfg<D>::NW; }
 
@@ -459,15 +462,26 @@ __global__ __launch_bounds__((64 * dkdv_waves<D, PRECISE, DQ_ATOMIC, DROP>()), D
                 sa[e] = c < lim ? -INFINITY : sa[e];
               }
             }
+            unsigned W[4];
+            if constexpr (DROP) drop_words_key_lane(dpar, bh, key, qs, g, lane, W);
   #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse2s[buf][32 * sb + 8 * i + 4 * g]);
+              f32x4 d4 = {};
+              if constexpr (DROP) d4 = *reinterpret_cast<const f32x4*>(&Ds[buf][32 * sb + 8 * i + 4 * g]);
   #pragma unroll
               for (int j = 0; j < 4; ++j) {
                 const int e = 4 * i + j;
                 const float p = fast_exp2(sa[e] * sl2 - l4[j]);
-                sa[e] = p;
-                pa[e] = p * pa[e];
+                if constexpr (DROP) {
+                  // kept: p (ks dP - D); dropped: -p D (d4 holds -D / ks)
+                  const bool keep = drop_keep(W, e, dpar.thresh);
+                  sa[e] = keep ? p : 0.f;
+                  pa[e] = (p * dpar.keep_scale) * (keep ? pa[e] : d4[j]);
+                } else {
+                  sa[e] = p;
+                  pa[e] = p * pa[e];
+                }
               }
             }
             bf16x8 pb[2], db[2];
